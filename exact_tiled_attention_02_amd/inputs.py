@@ -1,0 +1,176 @@
+"""Seeded synthetic inputs for exact tiled attention.
+
+This module is shared by the HIP path's tests and benchmark and by the CPU
+oracle's tests.  It draws random numbers and rounds them to the storage dtype;
+it contains none of the attention arithmetic.
+
+Recipe (the same for every workload):
+
+* ``rng = numpy.random.default_rng(seed)``; every tensor is drawn with
+  ``rng.standard_normal(shape, dtype=float32)`` in the order the workload
+  lists them (prefill: q, k, v; decode: seqlens first, then q, k-cache,
+  v-cache).
+* An optional query multiplier (3.0 for the Qwen3-0.6B-shaped workload, 100
+  for the stability case) is applied in fp32 *before* rounding.
+* bf16 storage rounds each fp32 value once, round-to-nearest-even, done with
+  integer bit arithmetic so the result does not depend on any library's
+  conversion routine.  The rounded bit patterns are what both the GPU and the
+  oracle consume.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# fp32 <-> bf16 storage conversion (bit arithmetic, round-to-nearest-even)
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (RNE) and return the 16-bit patterns (uint16)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    bias = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    r = ((u + bias) >> 16).astype(np.uint16)
+    if nan.any():
+        r = np.where(nan, ((u >> 16) | 0x0040).astype(np.uint16), r)
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to the fp32 values they encode (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+BF16_NAN = np.uint16(0x7FC0)
+
+
+# --------------------------------------------------------------------------
+# Workloads
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    """A forward (prefill) workload; q:[B,Hq,Tq,d], k,v:[B,Hkv,Tk,d]."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    Tk: int
+    d: int
+    causal: bool
+    dtype: str = "bf16"          # "bf16" or "f32"
+    q_mult: float = 1.0
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+    @property
+    def flops(self) -> float:
+        """Attention FLOPs, 4*B*Hq*Tq*Tk*d, halved for causal."""
+        f = 4.0 * self.B * self.Hq * self.Tq * self.Tk * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def min_bytes(self) -> int:
+        """Bytes that must cross HBM once: q, k, v read; o, lse written."""
+        es = 2 if self.dtype == "bf16" else 4
+        q = self.B * self.Hq * self.Tq * self.d * es
+        kv = 2 * self.B * self.Hkv * self.Tk * self.d * es
+        return 2 * q + kv + self.B * self.Hq * self.Tq * 4
+
+
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    """A single-query decode workload over a KV cache.
+
+    q:[B,Hq,d]; kcache,vcache:[B,Hkv,Tk_max,d]; seqlens:[B] int32 drawn
+    uniformly from [seq_lo, seq_hi] inclusive.
+    """
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Tk_max: int
+    d: int
+    seq_lo: int
+    seq_hi: int
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.d))
+
+
+# The five workloads the pages' hot path is measured on.
+SINGLE_HEAD_F32 = Prefill("single-head fp32 attention, T=256, d=64, non-causal",
+                          B=1, Hq=1, Hkv=1, Tq=256, Tk=256, d=64, causal=False,
+                          dtype="f32")
+GPT2_SMALL_MHA = Prefill("GPT-2-small MHA causal prefill, B=8, H=12, T=4096, d=64",
+                         B=8, Hq=12, Hkv=12, Tq=4096, Tk=4096, d=64, causal=True)
+QWEN3_0P6B_GQA = Prefill("Qwen3-0.6B GQA causal prefill, Hq=16, Hkv=8, T=4096, d=128, Qx3",
+                         B=1, Hq=16, Hkv=8, Tq=4096, Tk=4096, d=128, causal=True,
+                         q_mult=3.0)
+LLAMA3_8B_LONG = Prefill("Llama-3-8B GQA causal prefill, Hq=32, Hkv=8, T=32768, d=128",
+                         B=1, Hq=32, Hkv=8, Tq=32768, Tk=32768, d=128, causal=True)
+FLASH_DECODE = Decode("split-KV decode, B=16, Hq=32, Hkv=8, d=128, seqlen U[1024,32768]",
+                      B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768)
+
+WORKLOADS = {
+    "single_head_f32": SINGLE_HEAD_F32,
+    "gpt2_small_mha": GPT2_SMALL_MHA,
+    "qwen3_0p6b_gqa": QWEN3_0P6B_GQA,
+    "llama3_8b_long": LLAMA3_8B_LONG,
+    "flash_decode": FLASH_DECODE,
+}
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str, mult: float = 1.0) -> np.ndarray:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return x
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def prefill_inputs(w: Prefill, *, seed: Optional[int] = None):
+    """Return (q, k, v) as uint16 bf16 patterns or float32 arrays, row-major."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = _draw(rng, (w.B, w.Hq, w.Tq, w.d), w.dtype, w.q_mult)
+    k = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
+    v = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
+    return q, k, v
+
+
+def decode_seqlens(w: Decode, *, seed: Optional[int] = None) -> np.ndarray:
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    return rng.integers(w.seq_lo, w.seq_hi, w.B, endpoint=True).astype(np.int32)
+
+
+def decode_inputs(w: Decode, *, seed: Optional[int] = None, poison_tail: bool = False):
+    """Return (q, kcache, vcache, seqlens); q/caches as uint16 bf16 patterns.
+
+    With ``poison_tail`` every cache slot at or beyond seqlens[b] holds a bf16
+    NaN, so any read past the valid prefix shows up in the output.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    seqlens = rng.integers(w.seq_lo, w.seq_hi, w.B, endpoint=True).astype(np.int32)
+    q = _draw(rng, (w.B, w.Hq, w.d), "bf16")
+    kc = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "bf16")
+    vc = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "bf16")
+    if poison_tail:
+        for b, n in enumerate(seqlens):
+            kc[b, :, n:, :] = BF16_NAN
+            vc[b, :, n:, :] = BF16_NAN
+    return q, kc, vc, seqlens

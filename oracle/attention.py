@@ -1,0 +1,354 @@
+"""Plain fp64 CPU reference of exact attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package smoke check and the benchmark's CPU-baseline leg
+may import this module (see the package docstring for the page tags cited
+below).  It shares no code with the HIP library.
+
+What is computed.  The tiled method reaches exactly this result; it differs
+only in the order of floating-point additions ([FUSED07] section
+"FlashAttention-наив на numpy", opening paragraph; [LESSON] section "Почему
+ответ точный"):
+
+    s_ij  = scale * <q_i, k_j>          over the keys j visible to row i
+    O_i   = sum_j softmax_j(s_ij) * v_j
+    lse_i = log sum_j exp(s_ij)         ([LESSON] section "Обратный проход":
+                                         L_i = m_i + log l_i)
+
+Visibility of key j to query row i:
+
+    non-causal   every j < Tk
+    causal       j <= i -- top-left alignment, i.e. the strict upper triangle
+                 of the n x m score matrix is masked ([FUSED07],
+                 "FlashAttention-наив на numpy", reference attention)
+    decode       j < seqlens[b]; one query row; scale = 1/sqrt(d)
+
+Grouped-query attention: query head hq reads kv head hq // g, g = Hq / Hkv
+([NOTE] section "Prefill i dekodowanie to różne problemy": g query heads share
+one KV head).  This is the same as repeating every kv head g times.
+
+A row with no visible key (only possible for Tk == 0 or seqlen == 0) is
+defined as O = 0, lse = -inf.
+
+Arithmetic is IEEE fp64 throughout; inputs arrive as the exact bf16 bit
+patterns (uint16) or fp32 values that the GPU receives and are widened
+exactly.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence, Tuple
+
+import numpy as np
+
+_NEG_INF = -np.inf
+
+
+# --------------------------------------------------------------------------
+# Input widening
+# --------------------------------------------------------------------------
+
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Widen stored inputs to fp64 exactly.
+
+    uint16 arrays are bf16 bit patterns: the value is the fp32 whose upper 16
+    bits are the pattern and whose lower 16 bits are zero.
+    """
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if x.dtype in (np.float32, np.float64):
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+# --------------------------------------------------------------------------
+# Three-pass softmax attention (the definition, written out)
+# --------------------------------------------------------------------------
+
+def _rows_three_pass(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
+                     visible: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """softmax(scale * Qr K^T) V for a few rows, with a boolean visibility mask.
+
+    Pass 1 takes the row maximum of the visible scores, pass 2 sums
+    exp(s - m), pass 3 forms the exp-weighted sum of value rows and divides
+    once by that sum ([LESSON] section "Online softmax: нормировка за один
+    проход" describes this three-pass stable softmax that the online form
+    replaces).
+    """
+    n = Qr.shape[0]
+    dv = V.shape[1]
+    O = np.zeros((n, dv))
+    lse = np.full(n, _NEG_INF)
+    if K.shape[0] == 0:
+        return O, lse
+    S = (Qr @ K.T) * scale
+    S = np.where(visible, S, _NEG_INF)
+    m = S.max(axis=1)                                   # pass 1
+    has = np.isfinite(m)
+    if not has.any():
+        return O, lse
+    with np.errstate(invalid="ignore"):
+        E = np.exp(S[has] - m[has, None])              # pass 2
+    l = E.sum(axis=1)
+    O[has] = (E @ V) / l[:, None]                       # pass 3
+    lse[has] = m[has] + np.log(l)
+    return O, lse
+
+
+def softmax_attention(q, k, v, *, causal: bool, scale: float,
+                      row_chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact attention for q:[B,Hq,Tq,d], k,v:[B,Hkv,Tk,d] -> (O, lse) in fp64.
+
+    Rows are independent, so they are evaluated in chunks of ``row_chunk`` to
+    bound memory; under the causal mask a chunk ending at row r only needs
+    keys j <= r, so the keys beyond are left out (every one of them would be
+    masked to -inf and contribute exp(-inf) = 0).
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    if (Bk, dk) != (B, d) or v.shape[:3] != k.shape[:3] or Hq % max(Hkv, 1):
+        raise ValueError("shape mismatch")
+    g = Hq // Hkv
+    O = np.zeros((B, Hq, Tq, v.shape[3]))
+    L = np.full((B, Hq, Tq), _NEG_INF)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            for r0 in range(0, Tq, row_chunk):
+                r1 = min(Tq, r0 + row_chunk)
+                kend = min(Tk, r1) if causal else Tk
+                rows = np.arange(r0, r1)[:, None]
+                cols = np.arange(kend)[None, :]
+                vis = (cols <= rows) if causal else np.ones((r1 - r0, kend), bool)
+                O[b, h, r0:r1], L[b, h, r0:r1] = _rows_three_pass(
+                    q[b, h, r0:r1], k[b, kh, :kend], v[b, kh, :kend], scale, vis)
+    return O, L
+
+
+def softmax_attention_rows(q, k, v, *, causal: bool, scale: float, b: int, h: int,
+                           rows: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """The same definition evaluated for selected query rows of one (b, h).
+
+    Used where the full output is too large to check against one by one.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    Hq = q.shape[1]
+    Hkv = k.shape[1]
+    kh = h // (Hq // Hkv)
+    Qr = as_f64(q[b, h, rows])
+    K = as_f64(k[b, kh])
+    V = as_f64(v[b, kh])
+    cols = np.arange(K.shape[0])[None, :]
+    vis = (cols <= rows[:, None]) if causal else np.ones((len(rows), K.shape[0]), bool)
+    return _rows_three_pass(Qr, K, V, scale, vis)
+
+
+# --------------------------------------------------------------------------
+# The online (tiled) fold -- a second, independent route to the same result
+# --------------------------------------------------------------------------
+
+def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
+                          Bc: int = 64, count: bool = False):
+    """FlashAttention forward in fp64, FA-2 loop order.
+
+    Follows [LESSON] section "Прямой проход FlashAttention" and [FUSED07]
+    section "Online softmax: вывод": for each block of Br query rows keep a
+    running max m, a running sum l and an unnormalised accumulator A; for
+    each block of Bc keys
+
+        S  = scale * Q_i K_j^T           (masked entries -> -inf, before max)
+        m' = max(m, rowmax S)
+        P  = exp(S - m')
+        l  = l * exp(m - m') + rowsum P
+        A  = A * exp(m - m') + P V_j,    m = m'
+
+    and after the last block O = A / l (one division per row) and
+    lse = m + log l.  Under the causal mask key blocks that start after the
+    last row of the query block are skipped ([FUSED07] section
+    "FlashAttention-2", change 3).  Returns (O, lse) or, with ``count``,
+    (O, lse, visited_block_pairs).
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    dv = v.shape[3]
+    O = np.zeros((B, Hq, Tq, dv))
+    L = np.full((B, Hq, Tq), _NEG_INF)
+    pairs = 0
+    for b in range(B):
+        for h in range(Hq):
+            K = k[b, h // g]
+            V = v[b, h // g]
+            for i0 in range(0, Tq, Br):
+                Qi = q[b, h, i0:i0 + Br]
+                n = Qi.shape[0]
+                i_last = i0 + n - 1
+                m = np.full(n, _NEG_INF)
+                l = np.zeros(n)
+                A = np.zeros((n, dv))
+                for j0 in range(0, Tk, Bc):
+                    if causal and j0 > i_last:
+                        break
+                    pairs += 1
+                    Kj = K[j0:j0 + Bc]
+                    Vj = V[j0:j0 + Bc]
+                    S = (Qi @ Kj.T) * scale
+                    if causal:
+                        rows = np.arange(i0, i0 + n)[:, None]
+                        cols = np.arange(j0, j0 + Kj.shape[0])[None, :]
+                        S = np.where(cols > rows, _NEG_INF, S)
+                    m_new = np.maximum(m, S.max(axis=1))
+                    # A row that has seen no visible key keeps m' = -inf; its
+                    # sums stay zero (exp of -inf), so subtract 0 instead.
+                    ref = np.where(np.isfinite(m_new), m_new, 0.0)
+                    corr = np.exp(m - ref)
+                    P = np.exp(S - ref[:, None])
+                    l = l * corr + P.sum(axis=1)
+                    A = A * corr[:, None] + P @ Vj
+                    m = m_new
+                ok = l > 0
+                O[b, h, i0:i0 + n][ok] = A[ok] / l[ok, None]
+                L[b, h, i0:i0 + n][ok] = m[ok] + np.log(l[ok])
+    if count:
+        return O, L, pairs
+    return O, L
+
+
+def causal_block_pairs(Tq: int, Tk: int, Br: int, Bc: int, causal: bool) -> int:
+    """Number of (query block, key block) pairs the tiled loop visits.
+
+    All ceil(Tq/Br) * ceil(Tk/Bc) pairs without a mask; with the causal mask
+    only the pairs whose key block starts at or before the query block's last
+    row ([LESSON] practice template, ``count_blocks`` docstring).
+    """
+    n = 0
+    for i0 in range(0, Tq, Br):
+        i_last = min(Tq, i0 + Br) - 1
+        for j0 in range(0, Tk, Bc):
+            if causal and j0 > i_last:
+                break
+            n += 1
+    return n
+
+
+# --------------------------------------------------------------------------
+# Decode: one query per sequence over a KV cache
+# --------------------------------------------------------------------------
+
+def decode_attention(q, kcache, vcache, seqlens) -> Tuple[np.ndarray, np.ndarray]:
+    """Single-query attention over each sequence's valid cache prefix.
+
+    q:[B,Hq,d]; kcache,vcache:[B,Hkv,Tk_max,d]; seqlens:[B].  Key j of
+    sequence b is visible iff j < seqlens[b]; scale = 1/sqrt(d); no other mask.
+    Cache slots at or beyond seqlens[b] are never read.  Returns (O[B,Hq,d],
+    lse[B,Hq]) in fp64.
+    """
+    B, Hq, d = q.shape
+    Hkv = kcache.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, vcache.shape[3]))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in range(B):
+        n = int(seqlens[b])
+        for h in range(Hq):
+            K = as_f64(kcache[b, h // g, :n])
+            V = as_f64(vcache[b, h // g, :n])
+            Qr = as_f64(q[b, h])[None, :]
+            o, lse = _rows_three_pass(Qr, K, V, scale, np.ones((1, n), bool))
+            O[b, h], L[b, h] = o[0], lse[0]
+    return O, L
+
+
+def decode_split_merge(q, kcache, vcache, seqlens, num_splits: int,
+                       tile: int = 64) -> Tuple[np.ndarray, np.ndarray]:
+    """Flash-decoding in fp64: split each sequence's keys, merge the partials.
+
+    [NOTE] section "Prefill i dekodowanie to różne problemy" (Flash-decoding):
+    with one query there are no rows to spread over blocks, so the key
+    sequence is cut into pieces; each piece yields a partial (m, l, o) and a
+    last step merges them with the same rescaling rule.  Sequence b is cut
+    into chunks of c = tile * ceil(ceil(seqlens[b] / num_splits) / tile) keys;
+    chunks that start at or past seqlens[b] are empty (m = -inf, l = 0).
+
+    Merge ([BOOK5] section 5.3.3, Example 5-6 and the update equations after
+    it): M = max_s m_s, l = sum_s exp(m_s - M) l_s,
+    o = sum_s exp(m_s - M) o_s, O = o / l; empty pieces drop out because
+    their weight is exp(-inf) = 0 and their sums are 0.
+    """
+    B, Hq, d = q.shape
+    Hkv = kcache.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, vcache.shape[3]))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in range(B):
+        n = int(seqlens[b])
+        per = -(-n // num_splits)
+        c = tile * (-(-per // tile)) if n > 0 else tile
+        for h in range(Hq):
+            Qv = as_f64(q[b, h])
+            parts = []
+            for s in range(num_splits):
+                lo, hi = s * c, min(n, (s + 1) * c)
+                if lo >= hi:
+                    parts.append((_NEG_INF, 0.0, np.zeros(vcache.shape[3])))
+                    continue
+                K = as_f64(kcache[b, h // g, lo:hi])
+                V = as_f64(vcache[b, h // g, lo:hi])
+                sc = (K @ Qv) * scale
+                m_s = sc.max()
+                e = np.exp(sc - m_s)
+                parts.append((m_s, e.sum(), e @ V))
+            ms = np.array([p[0] for p in parts])
+            if not np.isfinite(ms).any():
+                continue
+            M = ms.max()
+            w = np.exp(ms - M)
+            l = sum(w[s] * parts[s][1] for s in range(num_splits))
+            o = sum(w[s] * parts[s][2] for s in range(num_splits))
+            O[b, h] = o / l
+            L[b, h] = M + math.log(l)
+    return O, L
+
+
+# --------------------------------------------------------------------------
+# Scalar online normaliser (element by element)
+# --------------------------------------------------------------------------
+
+def online_normalizer(xs: Iterable[float]) -> Tuple[float, float]:
+    """One pass over xs giving m = max x and l = sum exp(x - m).
+
+    [LESSON] section "Online softmax: нормировка за один проход":
+    m' = max(m, x), l' = l * exp(m - m') + exp(x - m'), from m = -inf, l = 0.
+    """
+    m, l = -math.inf, 0.0
+    for x in xs:
+        m_new = max(m, x)
+        l = l * math.exp(m - m_new) + math.exp(x - m_new)
+        m = m_new
+    return m, l
+
+
+def online_weighted_sum(xs: Sequence[float], vs: Sequence) -> Tuple[float, float, np.ndarray, np.ndarray]:
+    """One pass giving (m, l, a, o) with a = sum exp(x - m) v and o = a / l.
+
+    Same section as ``online_normaliser``: a' = a * exp(m - m') + exp(x - m') v,
+    divided by l once at the end.
+    """
+    m, l = -math.inf, 0.0
+    a = np.zeros_like(np.asarray(vs[0], dtype=np.float64))
+    for x, v in zip(xs, vs):
+        m_new = max(m, x)
+        r = math.exp(m - m_new)
+        p = math.exp(x - m_new)
+        l = l * r + p
+        a = a * r + p * np.asarray(v, dtype=np.float64)
+        m = m_new
+    return m, l, a, a / l
