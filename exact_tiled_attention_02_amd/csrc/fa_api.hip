@@ -1,0 +1,205 @@
+// C ABI of the exact tiled attention library (declared in include/fa.h):
+// argument validation, launch planning and the decode workspace.
+#include <math.h>
+#include <stdint.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+// Keyed by (device, stream): calls on one stream are ordered by the stream,
+// so a buffer is never used by two calls at once.
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int map_err(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+int check_fwd(const void* q, const void* k, const void* v, const void* o, int B, int Hq, int Hkv,
+              int Tq, int Tk, int d, float scale, bool* empty) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  *empty = (B == 0 || Hq == 0 || Tq == 0);
+  if (*empty) return FA_OK;
+  if (q == nullptr || o == nullptr) return FA_ERR_NULL;
+  if (Tk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
+  // Offsets are formed in 64-bit; per-dimension products that index one
+  // (batch, head) plane must stay within int range.
+  if ((int64_t)Tq * d > INT32_MAX || (int64_t)Tk * d > INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
+  // Query tiles run along grid.y (at most 65535 of them, 32 rows or more each).
+  if (Tq > 65535 * 32) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+fa::FwdParams make_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Hq, int Hkv, int Tq, int Tk, int d, float scale) {
+  fa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.g = Hq / Hkv;
+  p.groups = p.g;
+  // Scores become base-2 exponents s * |scale| * log2(e); a negative scale
+  // is folded into the sign of q (exact), and |scale| is kept away from 0 so
+  // that masked (-inf) scores still map to -inf rather than NaN.  Below
+  // 1e-30 every visible probability is exactly 1 in fp32 either way.
+  const double a = fabs((double)scale);
+  p.c = (float)(fmax(a, 1e-30) * 1.4426950408889634);
+  p.negate_q = scale < 0.f ? 1 : 0;
+  (void)d;
+  return p;
+}
+
+int auto_splits(int B, int Hkv, int Tk_max) {
+  // Enough workgroups to cover the 256 compute units several times over,
+  // with pieces of at least 256 keys.
+  const int64_t units = (int64_t)B * Hkv;
+  int64_t s = (2048 + units - 1) / units;
+  const int64_t cap = (Tk_max + 255) / 256;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+int clamp_splits(int B, int Hkv, int Tk_max, int num_splits) {
+  int s = num_splits == 0 ? auto_splits(B, Hkv, Tk_max) : num_splits;
+  const int cap = (Tk_max + fa::kDecodeTile - 1) / fa::kDecodeTile;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+           int Tq, int Tk, int d, int causal, float scale, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale);
+  return map_err(fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
+               int Hkv, int Tq, int Tk, int d, int causal, float scale, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale);
+  return map_err(fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
+}
+
+int fa_decode_splits(int B, int Hkv, int Tk_max, int d, int num_splits) {
+  (void)d;
+  if (B < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return 1;
+  return clamp_splits(B, Hkv, Tk_max, num_splits);
+}
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens, void* o,
+              int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Hq == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || seqlens == nullptr) return FA_ERR_NULL;
+  if (Tk_max > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_NULL;
+  // Sequences run along grid.z and kv heads along grid.y.
+  if (B > 65535 || Hkv > 65535 || (int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
+
+  const int S = clamp_splits(B, Hkv, Tk_max, num_splits);
+  const size_t nparts = (size_t)B * Hq * S;
+  const size_t need = nparts * (size_t)(d + 2) * sizeof(float);
+  hipStream_t hs = (hipStream_t)stream;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[std::make_pair(dev, hs)];
+    if (w.bytes < need) {
+      if (w.ptr != nullptr) {
+        if (hipFreeAsync(w.ptr, hs) != hipSuccess) return FA_ERR_ALLOC;
+        w.ptr = nullptr;
+        w.bytes = 0;
+      }
+      size_t grow = need + need / 4;
+      if (hipMallocAsync(&w.ptr, grow, hs) != hipSuccess) {
+        w.ptr = nullptr;
+        return FA_ERR_ALLOC;
+      }
+      w.bytes = grow;
+    }
+    ws = w.ptr;
+  }
+
+  fa::DecodeParams p{};
+  p.q = q;
+  p.kcache = kcache;
+  p.vcache = vcache;
+  p.seqlens = seqlens;
+  p.o = o;
+  p.part_m = (float*)ws;
+  p.part_l = p.part_m + nparts;
+  p.part_o = p.part_l + nparts;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tk_max = Tk_max;
+  p.g = Hq / Hkv;
+  p.splits = S;
+  p.c = (float)(1.4426950408889634 / sqrt((double)d));
+  return map_err(fa::launch_decode(p, d, hs));
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape or size argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128)";
+    case FA_ERR_ALLOC: return "decode workspace allocation failed";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+  }
+}
+
+void fa_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  (void)hipGetDevice(&cur);
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr != nullptr) {
+      // hipFree (not the stream-ordered form): the stream a buffer was
+      // grown on may no longer exist.
+      (void)hipSetDevice(kv.first.first);
+      (void)hipFree(kv.second.ptr);
+    }
+  }
+  g_ws.clear();
+  (void)hipSetDevice(cur);
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+"""Python binding of the HIP library ``libfa.so`` (argument marshalling only).
+
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_decode``, ``fa_decode_splits``,
+``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
+``include/fa.h`` one to one: pointers may be given as integers or as objects
+with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
+default stream) or objects with a ``cuda_stream`` attribute.  A nonzero
+status raises :class:`FAError`.
+
+``attention`` and ``decode`` are conveniences for torch tensors: they check
+dtypes/shapes/contiguity, allocate the outputs with torch and call the entry
+points above.  Every step of the computation runs in the HIP kernels; if the
+library is not built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+                4: "FA_ERR_ALLOC", 5: "FA_ERR_LAUNCH", 6: "FA_ERR_DEVICE"}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({fa_strerror(status)})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with "
+                              "`python -m exact_tiled_attention_02_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.fa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        lib.fa_fwd.restype = I
+        lib.fa_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        lib.fa_fwd_f32.restype = I
+        lib.fa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.fa_decode.restype = I
+        lib.fa_decode_splits.argtypes = [I, I, I, I, I]
+        lib.fa_decode_splits.restype = I
+        lib.fa_strerror.argtypes = [I]
+        lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_release_workspace.argtypes = []
+        lib.fa_release_workspace.restype = None
+        _lib = lib
+        return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    dp = getattr(x, "data_ptr", None)
+    if dp is not None:
+        return dp()
+    raise TypeError(f"cannot take a device pointer from {type(x).__name__}")
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    cs = getattr(s, "cuda_stream", None)
+    if cs is not None:
+        return cs
+    raise TypeError(f"cannot take a stream handle from {type(s).__name__}")
+
+
+def _check(st: int, where: str) -> None:
+    if st != FA_OK:
+        raise FAError(st, where)
+
+
+# --- one-to-one entry points -------------------------------------------------
+
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
+    _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
+                         int(bool(causal)), float(scale), _stream(stream)), "fa_fwd")
+
+
+def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
+    _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk,
+                             d, int(bool(causal)), float(scale), _stream(stream)), "fa_fwd_f32")
+
+
+def fa_decode(q, kcache, vcache, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits, stream=None) -> None:
+    _check(load().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o), B, Hq,
+                            Hkv, Tk_max, d, int(num_splits), _stream(stream)), "fa_decode")
+
+
+def fa_decode_splits(B, Hkv, Tk_max, d, num_splits) -> int:
+    return load().fa_decode_splits(B, Hkv, Tk_max, d, int(num_splits))
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(int(status)).decode()
+
+
+def fa_release_workspace() -> None:
+    load().fa_release_workspace()
+
+
+# --- torch conveniences --------------------------------------------------------
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def attention(q, k, v, *, causal: bool, scale: float | None = None, return_lse: bool = True,
+              out=None, lse=None, stream=None):
+    """softmax(q k^T * scale) v for contiguous [B,H,T,d] cuda tensors.
+
+    bf16 inputs use ``fa_fwd``; fp32 inputs use ``fa_fwd_f32``.  Returns
+    (o, lse) or o.
+    """
+    import torch
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be [B,H,T,d]")
+    _require(q.is_cuda and k.is_cuda and v.is_cuda, "tensors must live on the GPU")
+    _require(q.dtype == k.dtype == v.dtype and q.dtype in (torch.bfloat16, torch.float32),
+             "q, k, v must all be bf16 or all fp32")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(), "tensors must be contiguous")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk = k.shape
+    _require(Bk == B and dk == d and tuple(v.shape) == tuple(k.shape), "shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
+    fn(q, k, v, out, lse if return_lse else None, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream)
+    return (out, lse) if return_lse else out
+
+
+def decode(q, kcache, vcache, seqlens, *, num_splits: int = 0, out=None, stream=None):
+    """Single-query attention over a KV cache; q [B,Hq,d], caches [B,Hkv,Tmax,d] bf16,
+    seqlens [B] int32 on the GPU."""
+    import torch
+    _require(q.dim() == 3 and kcache.dim() == 4 and vcache.shape == kcache.shape, "bad shapes")
+    _require(q.dtype == kcache.dtype == vcache.dtype == torch.bfloat16, "decode takes bf16")
+    _require(seqlens.dtype == torch.int32 and seqlens.is_cuda, "seqlens must be int32 on the GPU")
+    _require(q.is_contiguous() and kcache.is_contiguous() and vcache.is_contiguous(),
+             "tensors must be contiguous")
+    B, Hq, d = q.shape
+    _, Hkv, Tmax, _ = kcache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fa_decode(q, kcache, vcache, seqlens, out, B, Hq, Hkv, Tmax, d, num_splits, stream)
+    return out

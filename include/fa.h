@@ -1,0 +1,142 @@
+/*
+ * fa.h -- exact tiled attention (FlashAttention forward and split-KV
+ * flash-decoding) for AMD Instinct MI355X (gfx950): the C ABI.
+ *
+ * Sources cited (web pages; sections named as headed there):
+ *   [FUSED07] "Модуль 07: Fused-операторы и FlashAttention" -- course
+ *             LLM Inference Systems, hermes-agent.ru.
+ *   [LESSON]  "FlashAttention: внимание без матрицы n×n" -- lesson 5.7.2,
+ *             ai.flicky.cc.
+ *   [NOTE]    "Atencja od strony jądra: FlashAttention, softmax online i
+ *             połączona dekwantyzacja" -- trefon.com notes.
+ *   [BOOK5]   "Глава 5. Операторы и среда выполнения" -- AI infra book,
+ *             bojieli.github.io.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous, row-major
+ *    buffer owned by the caller.  Inputs are only read; outputs are fully
+ *    overwritten.  The library never frees caller memory.
+ *  - bf16 buffers hold IEEE bfloat16 bit patterns (2 bytes per element).
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    (null) stream.  Calls enqueue work and return without waiting for it
+ *    ([BOOK5] section 5.1.3 "Stream, event и порядок завершения": launches
+ *    are asynchronous and the caller synchronises before reading results).
+ *    A fault inside a kernel therefore surfaces at the caller's next
+ *    synchronisation, not in the return code.
+ *  - Return value: FA_OK (0) or one of the fa_status codes below.  Argument
+ *    checks happen before any HIP call; on a nonzero return nothing has been
+ *    enqueued.
+ *  - Device addresses are not validated beyond non-NULL: passing buffers
+ *    smaller than the stated shapes is undefined behaviour.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,         /* a required pointer is NULL                      */
+  FA_ERR_SHAPE = 2,        /* negative size, Hq not a multiple of Hkv, ...    */
+  FA_ERR_UNSUPPORTED = 3,  /* head dimension other than 64 or 128             */
+  FA_ERR_ALLOC = 4,        /* the decode workspace could not be allocated     */
+  FA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch        */
+  FA_ERR_DEVICE = 6        /* no usable HIP device / runtime error            */
+} fa_status;
+
+/*
+ * fa_fwd -- exact attention forward pass (prefill), bf16 in/out.
+ *
+ * Computes, for every batch b, query head hq, query row i:
+ *     s_ij   = scale * <q[b,hq,i,:], k[b,kh,j,:]>,   kh = hq / (Hq / Hkv)
+ *     o[b,hq,i,:] = sum_j softmax_j(s_ij) * v[b,kh,j,:]
+ *     lse[b,hq,i] = log sum_j exp(s_ij)              (natural log)
+ * over the keys j visible to row i: all j < Tk, or with causal != 0 only
+ * j <= i (top-left alignment when Tq != Tk).  This is softmax(Q K^T * scale) V
+ * computed tile by tile with the online softmax of [FUSED07] section
+ * "Online softmax: вывод" and the forward pass of [LESSON] section
+ * "Прямой проход FlashAttention"; neither the score matrix nor the
+ * probabilities are written to memory.  Grouped-query attention follows
+ * [NOTE] section "Prefill i dekodowanie to różne problemy" (g = Hq/Hkv query
+ * heads share kv head hq / g); lse is the per-row log-sum-exp
+ * L_i = m_i + log l_i of [LESSON] section "Обратный проход".
+ *
+ *   q   : [B, Hq,  Tq, d] bf16        k, v : [B, Hkv, Tk, d] bf16
+ *   o   : [B, Hq,  Tq, d] bf16 (rounded to nearest even)
+ *   lse : [B, Hq,  Tq] fp32, or NULL to skip it
+ *   d   : 64 or 128.  Any finite scale is accepted (1/sqrt(d) is usual).
+ *
+ * Arithmetic: q.k products and p.v products on bf16 matrix cores with fp32
+ * accumulation; the running max, sum and rescaling in fp32; the
+ * probabilities are rounded to bf16 before the p.v product.
+ * B == 0, Hq == 0 or Tq == 0 is a valid empty call.  Tk == 0 gives o = 0 and
+ * lse = -inf.  Errors: FA_ERR_NULL (q, k, v or o NULL on a non-empty call),
+ * FA_ERR_SHAPE (negative sizes, Hkv < 1, Hq % Hkv != 0, non-finite scale),
+ * FA_ERR_UNSUPPORTED (d not 64/128), FA_ERR_LAUNCH.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+           void* stream);
+
+/*
+ * fa_fwd_f32 -- the same operation and contract as fa_fwd with fp32 q, k, v
+ * and o.  Products and accumulation are fp32 (fp32 matrix cores); the
+ * probabilities stay fp32.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
+               void* stream);
+
+/*
+ * fa_decode -- single-query attention over a KV cache with split-KV
+ * flash-decoding ([NOTE] section "Prefill i dekodowanie to różne problemy",
+ * Flash-decoding paragraph): each sequence's valid keys are cut into
+ * num_splits contiguous pieces, every piece yields a partial (m, l, o) for
+ * the whole query-head group of its kv head, and a second kernel merges the
+ * partials with the rescaling rule of [BOOK5] section 5.3.3 (Example 5-6).
+ *
+ *   q       : [B, Hq, d] bf16 (one query token per sequence)
+ *   kcache  : [B, Hkv, Tk_max, d] bf16      vcache : same shape
+ *   seqlens : [B] int32, DEVICE memory; key j of sequence b is visible iff
+ *             j < seqlens[b].  Values are clamped to [0, Tk_max] on the
+ *             device; slots at or beyond seqlens[b] are never read.
+ *   o       : [B, Hq, d] bf16; a sequence with seqlens[b] == 0 gets o = 0.
+ *   scale is fixed at 1/sqrt(d).
+ *   num_splits: pieces per sequence.  0 lets the library choose from the
+ *             shape; a positive request is clamped to ceil(Tk_max / 64).
+ *             The result does not depend on the split count beyond
+ *             floating-point rounding, and for a fixed split count it is
+ *             bitwise reproducible (the merge runs in a fixed order,
+ *             [BOOK5] section 5.2.4 on split reductions and determinism).
+ *
+ * Workspace: the partials, B*Hq*splits*(d+2) fp32 values, live in a buffer
+ * the library owns per (device, stream), grown on demand with stream-ordered
+ * allocation on `stream` and kept for reuse.  Concurrent calls on the same
+ * stream are ordered by the stream; calls on different streams use
+ * different buffers.  fa_release_workspace() frees them.
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (negative sizes, Hq % Hkv != 0,
+ * num_splits < 0), FA_ERR_UNSUPPORTED (d not 64/128), FA_ERR_ALLOC,
+ * FA_ERR_LAUNCH.
+ */
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens,
+              void* o, int B, int Hq, int Hkv, int Tk_max, int d, int num_splits,
+              void* stream);
+
+/* The split count fa_decode uses for a request (after the 0 = automatic
+ * choice and the clamp), without launching anything. */
+int fa_decode_splits(int B, int Hkv, int Tk_max, int d, int num_splits);
+
+/* Static description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/* Frees every decode workspace the library holds.  The caller must make sure
+ * no fa_decode call is still executing on the device. */
+void fa_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA_H_ */

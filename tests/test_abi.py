@@ -1,0 +1,101 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_tiled_attention_02_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        from exact_tiled_attention_02_amd import build
+        build.build()
+    return fa.load()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_strerror", "fa_release_workspace",
+              "fa_decode_splits"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr), name
+
+
+P = None  # a NULL pointer
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale)
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 96, 1, 0.1), 3),      # d unsupported
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 3, 8, 8, 64, 1, 0.1), 2),      # Hq % Hkv
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 0, 8, 8, 64, 1, 0.1), 2),      # Hkv = 0
+    ((FAKE, FAKE, FAKE, FAKE, P, -1, 4, 2, 8, 8, 64, 1, 0.1), 2),     # negative B
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, -8, 8, 64, 1, 0.1), 2),     # negative Tq
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, -1, 64, 1, 0.1), 2),     # negative Tk
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, 1, float("nan")), 2),
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, 1, float("inf")), 2),
+    ((P, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, 1, 0.1), 1),         # q NULL
+    ((FAKE, P, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, 1, 0.1), 1),         # k NULL with Tk > 0
+    ((FAKE, FAKE, FAKE, P, P, 1, 4, 2, 8, 8, 64, 1, 0.1), 1),         # o NULL
+    ((P, P, P, P, P, 0, 4, 2, 8, 8, 64, 1, 0.1), 0),                  # empty batch: no-op
+    ((P, P, P, P, P, 2, 4, 2, 0, 8, 64, 0, 0.1), 0),                  # no query rows: no-op
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 1, 1, 65535 * 32 + 1, 8, 64, 1, 0.1), 2),  # too many rows
+])
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_validation(lib, entry, args, status):
+    fn = getattr(lib, entry)
+    assert fn(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, kc, vc, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits)
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 32, 4), 3),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 3, 64, 128, 4), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, -1), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, -5, 128, 4), 2),
+    ((FAKE, FAKE, FAKE, P, FAKE, 2, 8, 2, 64, 128, 4), 1),          # seqlens NULL
+    ((FAKE, P, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, 4), 1),          # kcache NULL
+    ((P, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, 4), 1),
+    ((P, P, P, P, P, 0, 8, 2, 64, 128, 4), 0),                      # empty batch
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 70000, 8, 2, 64, 128, 4), 2),   # B beyond grid.z
+])
+def test_decode_validation(lib, args, status):
+    assert lib.fa_decode(*args, None) == status
+
+
+def test_decode_split_planning(lib):
+    # Automatic choice for the 16-sequence, 8-kv-head cache of 32768 slots.
+    s = fa.fa_decode_splits(16, 8, 32768, 128, 0)
+    assert 1 <= s <= 32768 // 64
+    assert fa.fa_decode_splits(16, 8, 32768, 128, 16) == 16
+    assert fa.fa_decode_splits(16, 8, 32768, 128, 10**6) == 32768 // 64   # clamp
+    assert fa.fa_decode_splits(1, 1, 100, 128, 7) == 2                   # ceil(100/64)
+    assert fa.fa_decode_splits(1, 1, 0, 128, 7) == 1
+
+
+def test_strerror(lib):
+    for st in range(7):
+        assert fa.fa_strerror(st)
+    assert fa.fa_strerror(99) == "unknown status"
+    with pytest.raises(fa.FAError) as e:
+        fa.fa_fwd(FAKE, FAKE, FAKE, FAKE, None, 1, 4, 2, 8, 8, 96, True, 0.1)
+    assert e.value.status == 3
