@@ -53,25 +53,70 @@ constexpr int kBN = 64;  // keys per tile (bf16 kernel)
 // ---------------------------------------------------------------------------
 // LDS layouts of the bf16 kernel
 // ---------------------------------------------------------------------------
-
-// K tile: 64 key rows x D bf16; the 16-byte chunks of a row are XOR-permuted
-// so the 32 rows read by one half-wavefront land in distinct banks.
+// Both tiles are stored row-major, 64 key rows x D bf16, exactly as they sit
+// in HBM, and are filled by direct global->LDS copies (16 bytes per lane).
+// Only the order of the 16-byte chunks inside a row is permuted (XOR
+// swizzle), differently for the two tiles because they are read in
+// different patterns:
+//  * K is read 16 bytes per lane, 32 rows at one chunk position; the swizzle
+//    spreads 16 consecutive rows over all banks.
+//  * V is read through the transposing LDS read, 8 bytes per lane from 4
+//    consecutive rows; the swizzle moves those 4 rows to distinct banks.
 template <int D>
-__device__ __forceinline__ int k_off(int row, int chunk) {
-  constexpr int CPR = D / 8;
-  constexpr int R = CPR >= 16 ? 1 : 16 / CPR;
-  return row * D + ((chunk ^ ((row / R) % CPR)) << 3);
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// V^T tile: D rows (head dimension) x 64 keys; 8-byte slots of 4 keys are
-// XOR-permuted by the row index.
-__device__ __forceinline__ int vt_off(int drow, int slot) {
-  return drow * kBN + ((slot ^ ((drow >> 1) & 15)) << 2);
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pick16(const u32x4& w, int e) {
-  const uint32_t x = w[e >> 1];
-  return (e & 1) ? (x >> 16) : (x & 0xffffu);
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of
+// 16 lanes, output lane 4*q + e receives element e of the 8 bytes addressed
+// by input lanes q, q + 4, q + 8, q + 12 (in that order).  Issued as inline
+// assembly: through the compiler builtin every such read would first wait
+// for all outstanding global->LDS copies (which target the other LDS stage).
+// The result is not usable until lds_tr_wait() has run on it.
+__device__ __forceinline__ u32x2 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) const char lds_char_t;
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_char_t*)p;
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  return r;
+}
+// Wait until at most N LDS reads of this wavefront are outstanding (they
+// complete in issue order); the operand group passed in is tied to the wait
+// so its uses cannot be scheduled before it.
+template <int N, int ND>
+__device__ __forceinline__ void lds_tr_wait(u32x2 (&v)[ND][2]) {
+  static_assert(ND == 2 || ND == 4, "unexpected operand group");
+  if constexpr (ND == 4)
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[2][0]),
+                   "+v"(v[2][1]), "+v"(v[3][0]), "+v"(v[3][1])
+                 : "n"(N));
+  else
+    asm volatile("s_waitcnt lgkmcnt(%4)"
+                 : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[1][0]), "+v"(v[1][1])
+                 : "n"(N));
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -81,14 +126,12 @@ template <int D, bool CAUSAL, int HG>
 __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p) {
   constexpr int WPH = 4 / HG;        // wavefronts per query head
   constexpr int BMPOS = 32 * WPH;    // query positions per workgroup
-  constexpr int KT = kBN * D;        // elements of one K tile
-  constexpr int VT = D * kBN;        // elements of one V^T tile
+  constexpr int TILE = kBN * D;      // elements of one K or V tile
   constexpr int NC = D / 16;         // 16-deep steps of the Q.K product
   constexpr int ND = D / 32;         // 32-wide blocks of the output
-  constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
-  constexpr int NLD = kBN * CPR / kThreads;  // 16-byte loads per thread per tile
-  constexpr int RPL = kThreads / CPR;        // K rows covered by one load step
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * (KT + VT)];
+  constexpr int CPR = D / 8;         // 16-byte chunks per row
+  constexpr int NCOPY = TILE / 8 / kThreads;   // 16-byte copies per thread per tile
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE];   // [stage][K, V]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -131,41 +174,23 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
   const int kend = CAUSAL ? min(p.Tk, q_last) : p.Tk;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  u32x4 kreg[NLD], vreg[NLD];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto fetch = [&](int t0) {
+  // Issue the copies of key tile t0.. into LDS stage `stage`.  Copy r of
+  // wavefront w fills LDS chunks [(r*4 + w)*64, +64) of each tile; a chunk
+  // index L is row L / CPR, physical chunk L % CPR, which holds logical
+  // chunk (L % CPR) ^ swizzle(row).  Rows past the last key re-read the last
+  // key (finite data; those keys are masked).
+  auto issue_copies = [&](int t0, int stage) {
+    bf16* Ks = lds + stage * 2 * TILE;
+    bf16* Vs = Ks + TILE;
 #pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int key = t0 + r * RPL + tid / CPR;
-      kreg[r] = key < p.Tk ? *(const u32x4*)(Kg + (size_t)key * D + (tid % CPR) * 8) : zero4;
-    }
-#pragma unroll
-    for (int r = 0; r < NLD; ++r) {
-      const int key = t0 + (tid / CPR) * NLD + r;
-      vreg[r] = key < p.Tk ? *(const u32x4*)(Vg + (size_t)key * D + (tid % CPR) * 8) : zero4;
-    }
-  };
-  auto stash = [&](int stage) {
-    bf16* Ks = lds + stage * (KT + VT);
-    bf16* Vs = Ks + KT;
-#pragma unroll
-    for (int r = 0; r < NLD; ++r)
-      *(u32x4*)(Ks + k_off<D>(r * RPL + tid / CPR, tid % CPR)) = kreg[r];
-    // V^T: this thread holds NLD consecutive keys of one 8-wide d chunk.
-    const int kg = tid / CPR;
-    const int dch = (tid % CPR) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (NLD == 4) {
-        const uint32_t w0 = pick16(vreg[0], e) | (pick16(vreg[1], e) << 16);
-        const uint32_t w1 = pick16(vreg[2], e) | (pick16(vreg[3], e) << 16);
-        const u32x2 w = {w0, w1};
-        *(u32x2*)(Vs + vt_off(dch + e, kg)) = w;
-      } else {
-        static_assert(NLD == 2, "unexpected tile shape");
-        const uint32_t w0 = pick16(vreg[0], e) | (pick16(vreg[1], e) << 16);
-        *(uint32_t*)(Vs + vt_off(dch + e, kg >> 1) + ((kg & 1) << 1)) = w0;
-      }
+    for (int r = 0; r < NCOPY; ++r) {
+      const int base = (r * 4 + wave) * 64;      // first chunk of this copy
+      const int L = base + lane;
+      const int row = L / CPR;
+      const int pc = L % CPR;
+      const int key = min(t0 + row, p.Tk - 1);
+      copy16_to_lds(Kg + (size_t)key * D + ((pc ^ k_swz<D>(row)) << 3), Ks + base * 8);
+      copy16_to_lds(Vg + (size_t)key * D + ((pc ^ v_swz<D>(row)) << 3), Vs + base * 8);
     }
   };
 
@@ -178,17 +203,21 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  if (ntiles > 0) {
-    fetch(0);
-    stash(0);
-  }
+  // Per-lane constants of the transposing V reads (see lds_read_tr): input
+  // lane 4j + q of 16-lane group G reads 4 head-dim values starting at
+  // 16*(G%2) + 4q (+32*db) of key row r0 + j.
+  const int tr_j = (lane & 15) >> 2;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  if (ntiles > 0) issue_copies(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = t * kBN;
-    if (t + 1 < ntiles) fetch(t0 + kBN);
-    const bf16* Ks = lds + (t & 1) * (KT + VT);
-    const bf16* Vs = Ks + KT;
+    if (t + 1 < ntiles) issue_copies(t0 + kBN, (t + 1) & 1);
+    const bf16* Ks = lds + (t & 1) * 2 * TILE;
+    const bf16* Vs = Ks + TILE;
 
     // S^T for the tile's two 32-key blocks.  Under the causal mask a block
     // whose first key lies after this wavefront's last row is all masked.
@@ -200,9 +229,12 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       if (act[kb]) {
+        const int row = 32 * kb + col;
+        const bf16* kr = Ks + row * D;
+        const int sw = k_swz<D>(row);
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          const bf16x8 a = *(const bf16x8*)(Ks + k_off<D>(32 * kb + col, 2 * cc + half));
+          const bf16x8 a = *(const bf16x8*)(kr + (((2 * cc + half) ^ sw) << 3));
           s[kb] = mma_32x32x16(a, qf[cc], s[kb]);
         }
       }
@@ -222,63 +254,98 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
         }
     }
 
-    // Online softmax update for this row.
-    float mt = s[0][0];
+    // Row max of the tile (in-lane, then across the two wave halves).
+    float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = fmaxf(mt, swap_halves(mt));
+    for (int r = 1; r < 16; r += 2)
+      mt = fmaxf(mt, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
+    mt = fmaxf(mt, fmaxf(s[0][15], s[1][15]));
+    mt = max_halves(mt);
+
+    // Online update of the running max.  The accumulator is rescaled only
+    // when the max of some row of the wavefront actually grew ([FUSED07]
+    // "FlashAttention-2": rescale only if the maximum increased); l always
+    // takes its factor (exactly 1 where the max did not move).
     const float m_new = fmaxf(m, mt);
     const float corr = exp2_fast((m - m_new) * c);
-    const float mc = m_new * c;
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+#pragma unroll
+      for (int i = 0; i < ND; ++i) acc[i] *= corr;
+    }
+    l *= corr;
+    m = m_new;
+    const float mc = m * c;
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2_fast(fmaf(s[kb][r], c, -mc));
-        s[kb][r] = e;
-        ls += e;
+        s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mc));
+        ls += s[kb][r];
       }
-    l = l * corr + ls;
-    m = m_new;
-#pragma unroll
-    for (int i = 0; i < ND; ++i) acc[i] *= corr;
+    l += ls;
 
-    // O^T += V^T P^T.  The B operand for keys {16*j2 + 4*half + 0..3,
-    // 16*j2 + 8 + 4*half + 0..3} of block kb is s[kb][8*j2 .. 8*j2+7];
-    // the A operand reads V^T at the same keys.
+    // O^T += V^T P^T in four groups (kb, j2).  The B operand for keys
+    // {16*j2 + 4*half + 0..3, 16*j2 + 8 + 4*half + 0..3} of block kb is
+    // s[kb][8*j2 .. 8*j2+7]; the A operand holds V at the same keys for
+    // head-dim rows 32*db + col, read transposed from the row-major tile.
+    // The reads of group g+1 are in flight while group g multiplies.  A
+    // block that is entirely masked has probabilities 0 and is multiplied
+    // anyway (this happens only on the diagonal tile).
+    auto issue_v = [&](int kb, int j2, u32x2 (&v)[ND][2]) {
+      const int r_lo = 32 * kb + 16 * j2 + 4 * half + tr_j;
+      const int r_hi = r_lo + 8;
+      const bf16* v_lo = Vs + r_lo * D;
+      const bf16* v_hi = Vs + r_hi * D;
+      const int sw_lo = v_swz<D>(r_lo);
+      const int sw_hi = v_swz<D>(r_hi);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (!act[kb]) continue;
-#pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const bf16x2 two = to_bf16x2(s[kb][8 * j2 + i], s[kb][8 * j2 + i + 1]);
-          pb[i] = two[0];
-          pb[i + 1] = two[1];
-        }
-        const int slot = 8 * kb + 4 * j2 + half;
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const int drow = 32 * db + col;
-          const bf16x4 lo = *(const bf16x4*)(Vs + vt_off(drow, slot));
-          const bf16x4 hi = *(const bf16x4*)(Vs + vt_off(drow, slot + 2));
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          acc[db] = mma_32x32x16(a, pb, acc[db]);
-        }
+      for (int db = 0; db < ND; ++db) {
+        const int dd = 32 * db + tr_d;   // first of the 4 head-dim values this lane addresses
+        const int ch = dd >> 3;          // its 16-byte chunk
+        v[db][0] = lds_read_tr(v_lo + ((ch ^ sw_lo) << 3) + (dd & 7));
+        v[db][1] = lds_read_tr(v_hi + ((ch ^ sw_hi) << 3) + (dd & 7));
       }
+    };
+    auto multiply = [&](int kb, int j2, u32x2 (&v)[ND][2]) {
+      bf16x8 pb;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const bf16x2 two = to_bf16x2(s[kb][8 * j2 + i], s[kb][8 * j2 + i + 1]);
+        pb[i] = two[0];
+        pb[i + 1] = two[1];
+      }
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const u32x4 w = {v[db][0][0], v[db][0][1], v[db][1][0], v[db][1][1]};
+        bf16x8 a;
+        __builtin_memcpy(&a, &w, sizeof(a));
+        acc[db] = mma_32x32x16(a, pb, acc[db]);
+      }
+    };
+    {
+      constexpr int NR = 2 * ND;   // LDS reads per group
+      u32x2 va[ND][2], vb[ND][2];
+      issue_v(0, 0, va);
+      issue_v(0, 1, vb);
+      lds_tr_wait<NR>(va);
+      multiply(0, 0, va);
+      issue_v(1, 0, va);
+      lds_tr_wait<NR>(vb);
+      multiply(0, 1, vb);
+      issue_v(1, 1, vb);
+      lds_tr_wait<NR>(va);
+      multiply(1, 0, va);
+      lds_tr_wait<0>(vb);
+      multiply(1, 1, vb);
     }
 
-    if (t + 1 < ntiles) stash((t + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of the next tile have landed
     __syncthreads();
   }
 
   // Finalise: one division per row; lse in natural log.
-  const float lt = l + swap_halves(l);
+  const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (my_q < p.Tq) {
     bf16* Og = (bf16*)p.o + ((size_t)(b * p.Hq + hq) * p.Tq + my_q) * D;

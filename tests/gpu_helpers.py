@@ -36,6 +36,13 @@ def host_f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def check(name, got, want, tol):
+    """Assert max |got - want| <= tol and print the measured error."""
+    e = max_err(got, want)
+    print(f"  {name}: max|err| = {e:.3e} (bar {tol:.1e})", flush=True)
+    assert e <= tol, f"{name}: {e} > {tol}"
+
+
 def max_err(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import BF16_O_TOL, dev_bf16, host_bf16_as_f64, max_err, say
+from gpu_helpers import BF16_O_TOL, check, dev_bf16, host_bf16_as_f64, max_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,7 +58,7 @@ def test_decode_small(case, num_splits):
     say("fa_decode", case, "splits", num_splits)
     O = run_decode(q, kc, vc, sl, num_splits)
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
-    assert max_err(O, Or) <= BF16_O_TOL
+    check("O", O, Or, BF16_O_TOL)
     for b, n in enumerate(sl):
         if n == 0:
             assert np.all(O[b] == 0)
@@ -80,7 +80,7 @@ def test_flash_decode_workload_full(flash_decode_case, num_splits):
     q, kc, vc, sl, Or = flash_decode_case
     say("fa_decode", inputs.FLASH_DECODE.name, "splits", num_splits)
     O = run_decode(q, kc, vc, sl, num_splits)
-    assert max_err(O, Or) <= BF16_O_TOL
+    check("O", O, Or, BF16_O_TOL)
 
 
 def test_decode_deterministic_and_split_independent():
@@ -91,7 +91,7 @@ def test_decode_deterministic_and_split_independent():
     b = run_decode(q, kc, vc, sl, 5)
     assert np.array_equal(a, b)
     c = run_decode(q, kc, vc, sl, 31)
-    assert max_err(a, c) <= BF16_O_TOL
+    check("O", a, c, BF16_O_TOL)
 
 
 def test_decode_equals_single_row_forward():
@@ -109,4 +109,4 @@ def test_decode_equals_single_row_forward():
         o = torch.empty(1, 8, 1, 128, dtype=torch.bfloat16, device="cuda")
         fa.fa_fwd(tq, tk, tv, o, None, 1, 8, 2, 1, n, 128, False, 1 / math.sqrt(128))
         torch.cuda.synchronize()
-        assert max_err(O[b], host_bf16_as_f64(o)[0, :, 0]) <= BF16_O_TOL
+        check("O", O[b], host_bf16_as_f64(o)[0, :, 0], BF16_O_TOL)

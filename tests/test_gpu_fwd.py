@@ -11,8 +11,8 @@ import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import (BF16_LSE_TOL, BF16_O_TOL, F32_TOL, dev_bf16, dev_f32, host_bf16_as_f64,
-                         host_f64, max_err, say)
+from gpu_helpers import (BF16_LSE_TOL, BF16_O_TOL, F32_TOL, check, dev_bf16, dev_f32,
+                         host_bf16_as_f64, host_f64, max_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +81,8 @@ def test_bf16_small_shapes(shape):
     say("fa_fwd bf16", shape)
     O, L = run_bf16(q, k, v, causal, w.scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=causal, scale=w.scale)
-    assert max_err(O, Or) <= BF16_O_TOL
-    assert max_err(L, Lr) <= BF16_LSE_TOL
+    check("O", O, Or, BF16_O_TOL)
+    check("lse", L, Lr, BF16_LSE_TOL)
 
 
 @pytest.mark.parametrize("shape", SMALL[:10], ids=lambda s: "x".join(map(str, s)))
@@ -94,8 +94,8 @@ def test_f32_small_shapes(shape):
     say("fa_fwd_f32", shape)
     O, L = run_f32(q, k, v, causal, w.scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=causal, scale=w.scale)
-    assert max_err(O, Or) <= F32_TOL
-    assert max_err(L, Lr) <= F32_TOL
+    check("O", O, Or, F32_TOL)
+    check("lse", L, Lr, F32_TOL)
 
 
 def test_single_head_f32_workload():
@@ -105,8 +105,8 @@ def test_single_head_f32_workload():
     say("fa_fwd_f32", w.name)
     O, L = run_f32(q, k, v, w.causal, w.scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=w.causal, scale=w.scale)
-    assert max_err(O, Or) <= F32_TOL
-    assert max_err(L, Lr) <= F32_TOL
+    check("O", O, Or, F32_TOL)
+    check("lse", L, Lr, F32_TOL)
 
 
 def test_qwen3_gqa_workload_full():
@@ -116,8 +116,8 @@ def test_qwen3_gqa_workload_full():
     say("fa_fwd bf16", w.name)
     O, L = run_bf16(q, k, v, w.causal, w.scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=w.causal, scale=w.scale)
-    assert max_err(O, Or) <= BF16_O_TOL
-    assert max_err(L, Lr) <= BF16_LSE_TOL
+    check("O", O, Or, BF16_O_TOL)
+    check("lse", L, Lr, BF16_LSE_TOL)
 
 
 def _sample_rows(T, rng, n_random=192):
@@ -142,8 +142,8 @@ def test_full_size_workloads_sampled_rows(name):
         rows = _sample_rows(w.Tq, rng)
         Or, Lr = oracle.softmax_attention_rows(q, k, v, causal=w.causal, scale=w.scale, b=b, h=h,
                                                rows=rows)
-        assert max_err(O[b, h, rows], Or) <= BF16_O_TOL, (b, h)
-        assert max_err(L[b, h, rows], Lr) <= BF16_LSE_TOL, (b, h)
+        check("O", O[b, h, rows], Or, BF16_O_TOL)
+        check("lse", L[b, h, rows], Lr, BF16_LSE_TOL)
 
 
 def test_large_query_scale_stability():
@@ -155,9 +155,9 @@ def test_large_query_scale_stability():
     O, L = run_bf16(q, k, v, True, w.scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
-    assert max_err(O, Or) <= BF16_O_TOL
+    check("O", O, Or, BF16_O_TOL)
     # lse ~ 1e3 here; the bar is relative to fp32 rounding of such values.
-    assert max_err(L, Lr) <= max(BF16_LSE_TOL, 4e-6 * np.max(np.abs(Lr)))
+    check("lse", L, Lr, max(BF16_LSE_TOL, 4e-6 * np.max(np.abs(Lr))))
 
 
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
@@ -167,8 +167,8 @@ def test_other_scales(scale):
     say("fa_fwd bf16 scale", scale)
     O, L = run_bf16(q, k, v, True, scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=scale)
-    assert max_err(O, Or) <= BF16_O_TOL
-    assert max_err(L, Lr) <= BF16_LSE_TOL
+    check("O", O, Or, BF16_O_TOL)
+    check("lse", L, Lr, BF16_LSE_TOL)
 
 
 def test_no_keys_gives_zero_and_minus_inf():
@@ -215,4 +215,5 @@ def test_gqa_equals_repeated_heads_on_gpu():
     say("fa_fwd bf16 gqa vs mha")
     O1, L1 = run_bf16(q, k, v, True, w.scale)
     O2, L2 = run_bf16(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), True, w.scale)
-    assert max_err(O1, O2) <= BF16_O_TOL and max_err(L1, L2) <= BF16_LSE_TOL
+    check("O", O1, O2, BF16_O_TOL)
+    check("lse", L1, L2, BF16_LSE_TOL)
