@@ -186,6 +186,33 @@ def cpu_baseline(w, budget_s=12.0, max_s=30.0):
     }
 
 
+def inputs_names():
+    from exact_tiled_attention_02_amd import inputs
+    return inputs.WORKLOADS.keys()
+
+
+def run_only(torch, fa, inputs, args):
+    """One workload, `steps` timed calls, a one-line JSON summary."""
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+    w = inputs.WORKLOADS[args.only]
+    if isinstance(w, inputs.Prefill):
+        wall, ev = prefill_case(torch, fa, w, args.steps, args.warmup)
+        out = {"workload": w.name, "TFLOP/s": round(w.flops / wall / 1e12, 2),
+               "kernel_ms": round(ev, 4), "frac_of_mfma_peak": round(w.flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    else:
+        wall, ev, nbytes, _ = decode_case(torch, fa, w, args.steps, args.warmup, args.decode_splits)
+        out = {"workload": w.name, "GB/s": round(nbytes / (ev * 1e-3) / 1e9, 1),
+               "call_us": round(ev * 1e3, 2), "num_splits": args.decode_splits}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +221,11 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="num_splits for decode (0 = library choice)")
+    ap.add_argument("--only", choices=sorted(inputs_names()), default=None,
+                    help="time one workload only and print its numbers (for profiling runs)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="with --only: first run one device-to-device copy of this many MiB "
+                         "(the reference kernel for scaling traffic counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -207,6 +239,10 @@ def main():
     from exact_tiled_attention_02_amd import fa, inputs
     fa.load()
     torch.cuda.set_device(0)
+
+    if args.only is not None:
+        run_only(torch, fa, inputs, args)
+        return
 
     w = inputs.GPT2_SMALL_MHA
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")

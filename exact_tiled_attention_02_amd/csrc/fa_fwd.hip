@@ -41,6 +41,8 @@
 //    visited; only tiles crossing the diagonal (or the key tail) are masked,
 //    with -inf before the max ([FUSED07] task 07.2 pitfalls).  Workgroups
 //    are issued heaviest query tile first.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -53,15 +55,18 @@ constexpr int kBN = 64;  // keys per tile (bf16 kernel)
 // ---------------------------------------------------------------------------
 // LDS layouts of the bf16 kernel
 // ---------------------------------------------------------------------------
-// Both tiles are stored row-major, 64 key rows x D bf16, exactly as they sit
-// in HBM, and are filled by direct global->LDS copies (16 bytes per lane).
-// Only the order of the 16-byte chunks inside a row is permuted (XOR
-// swizzle), differently for the two tiles because they are read in
-// different patterns:
+// LDS holds [K stage 0 | K stage 1 | V stage 0 | V stage 1], each tile 64 key
+// rows x D bf16, row-major exactly as in HBM, filled by direct global->LDS
+// copies (16 bytes per lane).  Only the order of the 16-byte chunks inside a
+// row is permuted (XOR swizzle), differently for the two tiles because they
+// are read in different patterns:
 //  * K is read 16 bytes per lane, 32 rows at one chunk position; the swizzle
 //    spreads 16 consecutive rows over all banks.
 //  * V is read through the transposing LDS read, 8 bytes per lane from 4
 //    consecutive rows; the swizzle moves those 4 rows to distinct banks.
+// Both swizzles depend on row bits that are the same for every row a given
+// lane reads, so each lane's operand addresses are a fixed base plus
+// compile-time offsets.
 template <int D>
 __device__ __forceinline__ int k_swz(int row) {
   return D == 128 ? (row & 15) : ((row >> 1) & 7);
@@ -73,6 +78,23 @@ __device__ __forceinline__ int v_swz(int row) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) const char lds_char_t;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Calls f(IC<I>{}) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_char_t*)p;
+}
 
 // Copy 16 bytes per lane from global memory straight into LDS at
 // lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
@@ -80,19 +102,20 @@ __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each group of
-// 16 lanes, output lane 4*q + e receives element e of the 8 bytes addressed
-// by input lanes q, q + 4, q + 8, q + 12 (in that order).  Issued as inline
-// assembly: through the compiler builtin every such read would first wait
-// for all outstanding global->LDS copies (which target the other LDS stage).
-// The result is not usable until lds_tr_wait() has run on it.
-__device__ __forceinline__ u32x2 lds_read_tr(const bf16* p) {
-  typedef __attribute__((address_space(3))) const char lds_char_t;
-  const uint32_t a = (uint32_t)(uintptr_t)(lds_char_t*)p;
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16) at addr + OFF bytes:
+// within each group of 16 lanes, output lane 4*q + e receives element e of
+// the 8 bytes addressed by input lanes q, q + 4, q + 8, q + 12 (in that
+// order).  Issued as inline assembly: through the compiler builtin every such
+// read would first wait for all outstanding global->LDS copies (which target
+// the other LDS stage).  The result is not usable until lds_tr_wait() has
+// run on it.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
   u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+
 // Wait until at most N LDS reads of this wavefront are outstanding (they
 // complete in issue order); the operand group passed in is tied to the wait
 // so its uses cannot be scheduled before it.
@@ -131,7 +154,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
   constexpr int ND = D / 32;         // 32-wide blocks of the output
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NCOPY = TILE / 8 / kThreads;   // 16-byte copies per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE];   // [stage][K, V]
+  __shared__ __attribute__((aligned(16))) bf16 lds[4 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -174,25 +197,68 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
   const int kend = CAUSAL ? min(p.Tk, q_last) : p.Tk;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  // Issue the copies of key tile t0.. into LDS stage `stage`.  Copy r of
-  // wavefront w fills LDS chunks [(r*4 + w)*64, +64) of each tile; a chunk
-  // index L is row L / CPR, physical chunk L % CPR, which holds logical
-  // chunk (L % CPR) ^ swizzle(row).  Rows past the last key re-read the last
-  // key (finite data; those keys are masked).
-  auto issue_copies = [&](int t0, int stage) {
-    bf16* Ks = lds + stage * 2 * TILE;
-    bf16* Vs = Ks + TILE;
+  // Global->LDS copies.  Copy r of wavefront w fills LDS chunks
+  // [(r*4 + w)*64, +64) of a tile; chunk L is row L / CPR, physical chunk
+  // L % CPR, which holds logical chunk (L % CPR) ^ swizzle(row).  The source
+  // offsets within a tile are per-lane constants.
+  int ksrc[NCOPY], vsrc[NCOPY];
 #pragma unroll
-    for (int r = 0; r < NCOPY; ++r) {
-      const int base = (r * 4 + wave) * 64;      // first chunk of this copy
-      const int L = base + lane;
-      const int row = L / CPR;
-      const int pc = L % CPR;
-      const int key = min(t0 + row, p.Tk - 1);
-      copy16_to_lds(Kg + (size_t)key * D + ((pc ^ k_swz<D>(row)) << 3), Ks + base * 8);
-      copy16_to_lds(Vg + (size_t)key * D + ((pc ^ v_swz<D>(row)) << 3), Vs + base * 8);
+  for (int r = 0; r < NCOPY; ++r) {
+    const int L = (r * 4 + wave) * 64 + lane;
+    const int row = L / CPR;
+    const int pc = L % CPR;
+    ksrc[r] = row * D + ((pc ^ k_swz<D>(row)) << 3);
+    vsrc[r] = row * D + ((pc ^ v_swz<D>(row)) << 3);
+  }
+  auto issue_copies = [&](auto stage_c, int t0) {
+    constexpr int S = decltype(stage_c)::value;
+    bf16* Kd = lds + S * TILE;
+    bf16* Vd = lds + 2 * TILE + S * TILE;
+    if (t0 + kBN <= p.Tk) {
+      const bf16* kt = Kg + (size_t)t0 * D;
+      const bf16* vt = Vg + (size_t)t0 * D;
+#pragma unroll
+      for (int r = 0; r < NCOPY; ++r) {
+        copy16_to_lds(kt + ksrc[r], Kd + (r * 4 + wave) * 512);
+        copy16_to_lds(vt + vsrc[r], Vd + (r * 4 + wave) * 512);
+      }
+    } else {
+      // Tail tile: rows past the last key re-read the last key (finite
+      // data; those keys are masked).
+#pragma unroll
+      for (int r = 0; r < NCOPY; ++r) {
+        const int row = ((r * 4 + wave) * 64 + lane) / CPR;
+        const int key = min(t0 + row, p.Tk - 1);
+        copy16_to_lds(Kg + (size_t)key * D + (ksrc[r] - row * D), Kd + (r * 4 + wave) * 512);
+        copy16_to_lds(Vg + (size_t)key * D + (vsrc[r] - row * D), Vd + (r * 4 + wave) * 512);
+      }
     }
   };
+
+  // K operand read bases (stage 0, key block 0): stage S adds S*TILE and key
+  // block kb adds 32*kb*D elements.  k_swz of rows 32*kb + col is k_swz(col).
+  const bf16* kread[NC];
+  {
+    const int sw = k_swz<D>(col);
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) kread[cc] = lds + col * D + (((2 * cc + half) ^ sw) << 3);
+  }
+  // V operand bases for the transposing reads: input lane 4j + q of 16-lane
+  // group G addresses 4 head-dim values starting at 32*db + 16*(G%2) + 4q
+  // of key row 4*half + j (+ 32*kb + 16*j2 + 8*hi, a compile-time offset);
+  // v_swz is the same for all of those rows.
+  uint32_t vread[ND];
+  {
+    const int tr_j = (lane & 15) >> 2;
+    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int r0 = 4 * half + tr_j;
+    const int sw = v_swz<D>(r0);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int dd = 32 * db + tr_d;
+      vread[db] = lds_addr(lds + 2 * TILE + r0 * D + (((dd >> 3) ^ sw) << 3) + (dd & 7));
+    }
+  }
 
   const float c = p.c;
   float m = kNegInf;   // running max of this row's raw scores
@@ -203,42 +269,30 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  // Per-lane constants of the transposing V reads (see lds_read_tr): input
-  // lane 4j + q of 16-lane group G reads 4 head-dim values starting at
-  // 16*(G%2) + 4q (+32*db) of key row r0 + j.
-  const int tr_j = (lane & 15) >> 2;
-  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  if (ntiles > 0) issue_copies(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](auto stage_c, int t) {
+    constexpr int S = decltype(stage_c)::value;
     const int t0 = t * kBN;
-    if (t + 1 < ntiles) issue_copies(t0 + kBN, (t + 1) & 1);
-    const bf16* Ks = lds + (t & 1) * 2 * TILE;
-    const bf16* Vs = Ks + TILE;
+    if (t + 1 < ntiles) issue_copies(IC<1 - S>{}, t0 + kBN);
 
     // S^T for the tile's two 32-key blocks.  Under the causal mask a block
     // whose first key lies after this wavefront's last row is all masked.
     f32x16 s[2];
     bool act[2];
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       act[kb] = !CAUSAL || (t0 + 32 * kb <= q0w + 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
       if (act[kb]) {
-        const int row = 32 * kb + col;
-        const bf16* kr = Ks + row * D;
-        const int sw = k_swz<D>(row);
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          const bf16x8 a = *(const bf16x8*)(kr + (((2 * cc + half) ^ sw) << 3));
+          const bf16x8 a = *(const bf16x8*)(kread[cc] + S * TILE + kb * 32 * D);
           s[kb] = mma_32x32x16(a, qf[cc], s[kb]);
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // Mask (only tiles that cross the diagonal or the key tail): -inf
     // before the max, so masked keys get probability exactly 0.
@@ -257,7 +311,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
     // Row max of the tile (in-lane, then across the two wave halves).
     float mt = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; r += 2)
+    for (int r = 1; r < 15; r += 2)
       mt = fmaxf(mt, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
     mt = fmaxf(mt, fmaxf(s[0][15], s[1][15]));
     mt = max_halves(mt);
@@ -285,33 +339,29 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
       }
     l += ls;
 
-    // O^T += V^T P^T in four groups (kb, j2).  The B operand for keys
+    // O^T += V^T P^T in four groups g = (kb, j2).  The B operand for keys
     // {16*j2 + 4*half + 0..3, 16*j2 + 8 + 4*half + 0..3} of block kb is
     // s[kb][8*j2 .. 8*j2+7]; the A operand holds V at the same keys for
     // head-dim rows 32*db + col, read transposed from the row-major tile.
     // The reads of group g+1 are in flight while group g multiplies.  A
     // block that is entirely masked has probabilities 0 and is multiplied
     // anyway (this happens only on the diagonal tile).
-    auto issue_v = [&](int kb, int j2, u32x2 (&v)[ND][2]) {
-      const int r_lo = 32 * kb + 16 * j2 + 4 * half + tr_j;
-      const int r_hi = r_lo + 8;
-      const bf16* v_lo = Vs + r_lo * D;
-      const bf16* v_hi = Vs + r_hi * D;
-      const int sw_lo = v_swz<D>(r_lo);
-      const int sw_hi = v_swz<D>(r_hi);
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int dd = 32 * db + tr_d;   // first of the 4 head-dim values this lane addresses
-        const int ch = dd >> 3;          // its 16-byte chunk
-        v[db][0] = lds_read_tr(v_lo + ((ch ^ sw_lo) << 3) + (dd & 7));
-        v[db][1] = lds_read_tr(v_hi + ((ch ^ sw_hi) << 3) + (dd & 7));
-      }
+    auto issue_v = [&](auto g_c, u32x2 (&v)[ND][2]) {
+      constexpr int G = decltype(g_c)::value;
+      constexpr int OFF = (S * TILE + (32 * (G >> 1) + 16 * (G & 1)) * D) * 2;
+      static_for<0, ND>([&](auto db_c) {
+        constexpr int DB = decltype(db_c)::value;
+        v[DB][0] = lds_read_tr<OFF>(vread[DB]);
+        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vread[DB]);
+      });
     };
-    auto multiply = [&](int kb, int j2, u32x2 (&v)[ND][2]) {
+    auto multiply = [&](auto g_c, u32x2 (&v)[ND][2]) {
+      constexpr int G = decltype(g_c)::value;
+      constexpr int KB = G >> 1, J2 = G & 1;
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const bf16x2 two = to_bf16x2(s[kb][8 * j2 + i], s[kb][8 * j2 + i + 1]);
+        const bf16x2 two = to_bf16x2(s[KB][8 * J2 + i], s[KB][8 * J2 + i + 1]);
         pb[i] = two[0];
         pb[i + 1] = two[1];
       }
@@ -326,22 +376,32 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
     {
       constexpr int NR = 2 * ND;   // LDS reads per group
       u32x2 va[ND][2], vb[ND][2];
-      issue_v(0, 0, va);
-      issue_v(0, 1, vb);
+      issue_v(IC<0>{}, va);
+      issue_v(IC<1>{}, vb);
+      __builtin_amdgcn_s_setprio(1);
       lds_tr_wait<NR>(va);
-      multiply(0, 0, va);
-      issue_v(1, 0, va);
+      multiply(IC<0>{}, va);
+      issue_v(IC<2>{}, va);
       lds_tr_wait<NR>(vb);
-      multiply(0, 1, vb);
-      issue_v(1, 1, vb);
+      multiply(IC<1>{}, vb);
+      issue_v(IC<3>{}, vb);
       lds_tr_wait<NR>(va);
-      multiply(1, 0, va);
+      multiply(IC<2>{}, va);
       lds_tr_wait<0>(vb);
-      multiply(1, 1, vb);
+      multiply(IC<3>{}, vb);
+      __builtin_amdgcn_s_setprio(0);
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of the next tile have landed
     __syncthreads();
+  };
+
+  if (ntiles > 0) issue_copies(IC<0>{}, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    step(IC<0>{}, t);
+    if (t + 1 < ntiles) step(IC<1>{}, t + 1);
   }
 
   // Finalise: one division per row; lse in natural log.
