@@ -80,23 +80,23 @@ def dev_normal(torch, shape, gen, mult=1.0):
 
 
 def time_calls(torch, launch, steps: int, warmup: int):
-    """Run `launch` warmup times, then `steps` times bracketed by syncs.
-    Returns (wall seconds per call, mean event ms per call)."""
+    """Run `launch` warmup times, then `steps` times back to back, bracketed
+    by device synchronisation.  Returns (wall seconds per call, event ms per
+    call): HIP events recorded on the launch stream before the first and
+    after the last timed call give the average launch duration."""
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record()
+    start.record()
+    for _ in range(steps):
         launch()
-        ends[i].record()
+    end.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    ev = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / steps
-    return wall, ev
+    return wall, start.elapsed_time(end) / steps
 
 
 def prefill_case(torch, fa, w, steps, warmup, seed=0):
@@ -109,9 +109,8 @@ def prefill_case(torch, fa, w, steps, warmup, seed=0):
     lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def launch():
-        fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.causal, w.scale, stream)
-
+    launch = fa.prepared("fa_fwd", q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d,
+                         int(w.causal), w.scale, stream=stream)
     wall, ev_ms = time_calls(torch, launch, steps, warmup)
     del q, k, v, o, lse
     return wall, ev_ms
@@ -134,12 +133,13 @@ def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
     sl = torch.from_numpy(seqlens).cuda()
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
+    calls = [fa.prepared("fa_decode", q, kc, vc, sl, o, w.B, w.Hq, w.Hkv, w.Tk_max, w.d,
+                         num_splits, stream=stream) for kc, vc in caches]
     it = [0]
 
     def launch():
-        kc, vc = caches[it[0] % copies]
+        calls[it[0] % copies]()
         it[0] += 1
-        fa.fa_decode(q, kc, vc, sl, o, w.B, w.Hq, w.Hkv, w.Tk_max, w.d, num_splits, stream)
 
     wall, ev_ms = time_calls(torch, launch, steps, warmup)
     kv_bytes = int(seqlens.astype(np.int64).sum()) * w.Hkv * w.d * 2 * 2
@@ -216,8 +216,8 @@ def run_only(torch, fa, inputs, args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="num_splits for decode (0 = library choice)")
@@ -274,10 +274,10 @@ def main():
 
     if not args.no_extra:
         also = {}
-        for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 5)):
+        for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 10)):
             wk = inputs.WORKLOADS[name]
             log(f"[bench] {wk.name}")
-            wl, ev = prefill_case(torch, fa, wk, steps, 2)
+            wl, ev = prefill_case(torch, fa, wk, steps, max(2, min(args.warmup, steps)))
             ach = wk.flops / (ev * 1e-3) / 1e12
             also[name] = {"value": round(wk.flops / wl / 1e12, 2), "unit": "TFLOP/s",
                           "ms_per_call": round(wl * 1e3, 4), "kernel_ms": round(ev, 4),

@@ -36,7 +36,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
   if (Tk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_NULL;
   // Offsets are formed in 64-bit; per-dimension products that index one
   // (batch, head) plane must stay within int range.
-  if ((int64_t)Tq * d > INT32_MAX || (int64_t)Tk * d > INT32_MAX) return FA_ERR_SHAPE;
+  // K and V of one (batch, head) are addressed through 32-bit byte ranges.
+  if ((int64_t)Tq * d * 4 > INT32_MAX || (int64_t)Tk * d * 4 > INT32_MAX) return FA_ERR_SHAPE;
   if ((int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
   // Query tiles run along grid.y (at most 65535 of them, 32 rows or more each).
   if (Tq > 65535 * 32) return FA_ERR_SHAPE;

@@ -96,6 +96,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_char_t*)p;
 }
 
+// Copy 16 bytes per lane from a buffer resource (byte offset voff + soff;
+// past the resource's size the data read is zero) straight into LDS at
+// lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void copy16_buf_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
+}
+
 // Copy 16 bytes per lane from global memory straight into LDS at
 // lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
 __device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_base) {
@@ -133,6 +141,14 @@ __device__ __forceinline__ void lds_tr_wait(u32x2 (&v)[ND][2]) {
                  : "n"(N));
 }
 
+// s_waitcnt immediate that waits for the vector-memory counter to drop to N
+// and leaves the other counters unconstrained.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -145,20 +161,29 @@ __device__ __forceinline__ float sum_halves(float x) {
 // ---------------------------------------------------------------------------
 // bf16 forward kernel
 // ---------------------------------------------------------------------------
+// A workgroup is 8 wavefronts (two per SIMD); each wavefront owns 32 query
+// rows of one query head and all 8 share every K/V tile staged in LDS.  LDS
+// holds kStages K tiles and kStages V tiles; the copy of tile t+3 is issued
+// while tile t is computed, so a copy has three iterations to land.
+constexpr int kFwdThreads = 512;
+constexpr int kStages = 4;
+
 template <int D, bool CAUSAL, int HG>
-__global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p) {
-  constexpr int WPH = 4 / HG;        // wavefronts per query head
+__global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParams p) {
+  constexpr int NW = kFwdThreads / 64;
+  constexpr int WPH = NW / HG;       // wavefronts per query head
   constexpr int BMPOS = 32 * WPH;    // query positions per workgroup
   constexpr int TILE = kBN * D;      // elements of one K or V tile
   constexpr int NC = D / 16;         // 16-deep steps of the Q.K product
   constexpr int ND = D / 32;         // 32-wide blocks of the output
   constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int NCOPY = TILE / 8 / kThreads;   // 16-byte copies per thread per tile
-  __shared__ __attribute__((aligned(16))) bf16 lds[4 * TILE];
+  constexpr int NCOPY = TILE / 8 / kFwdThreads;   // 16-byte copies per thread per tile and tensor
+  static_assert(NCOPY >= 1, "tile too small for the workgroup");
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStages * TILE];   // K0..K3 | V0..V3
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
 
@@ -197,51 +222,55 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
   const int kend = CAUSAL ? min(p.Tk, q_last) : p.Tk;
   const int ntiles = (kend + kBN - 1) / kBN;
 
-  // Global->LDS copies.  Copy r of wavefront w fills LDS chunks
-  // [(r*4 + w)*64, +64) of a tile; chunk L is row L / CPR, physical chunk
-  // L % CPR, which holds logical chunk (L % CPR) ^ swizzle(row).  The source
-  // offsets within a tile are per-lane constants.
-  int ksrc[NCOPY], vsrc[NCOPY];
+  // Global->LDS copies through buffer resources covering this head's K and
+  // V: reads past the last key return zeros (finite; those keys are masked).
+  // Copy r of wavefront w fills LDS chunks [(r*NW + w)*64, +64) of a tile;
+  // chunk L is row L / CPR, physical chunk L % CPR, which holds logical
+  // chunk (L % CPR) ^ swizzle(row).  Lane byte offsets within a tile are
+  // constants; the tile start is a scalar offset.
+  const int nbytes = p.Tk * D * 2;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, nbytes, 0x00020000);
+  uint32_t ksrc[NCOPY], vsrc[NCOPY];
 #pragma unroll
   for (int r = 0; r < NCOPY; ++r) {
-    const int L = (r * 4 + wave) * 64 + lane;
+    const int L = (r * NW + wave) * 64 + lane;
     const int row = L / CPR;
     const int pc = L % CPR;
-    ksrc[r] = row * D + ((pc ^ k_swz<D>(row)) << 3);
-    vsrc[r] = row * D + ((pc ^ v_swz<D>(row)) << 3);
+    ksrc[r] = (uint32_t)(row * D + ((pc ^ k_swz<D>(row)) << 3)) * 2u;
+    vsrc[r] = (uint32_t)(row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2u;
   }
-  auto issue_copies = [&](auto stage_c, int t0) {
-    constexpr int S = decltype(stage_c)::value;
-    bf16* Kd = lds + S * TILE;
-    bf16* Vd = lds + 2 * TILE + S * TILE;
-    if (t0 + kBN <= p.Tk) {
-      const bf16* kt = Kg + (size_t)t0 * D;
-      const bf16* vt = Vg + (size_t)t0 * D;
+  auto issue_copies = [&](int t) {   // tile t into stage t % kStages
+    const int st = t % kStages;
+    const uint32_t soff = (uint32_t)t * kBN * D * 2;
+    bf16* Kd = lds + st * TILE;
+    bf16* Vd = lds + (kStages + st) * TILE;
 #pragma unroll
-      for (int r = 0; r < NCOPY; ++r) {
-        copy16_to_lds(kt + ksrc[r], Kd + (r * 4 + wave) * 512);
-        copy16_to_lds(vt + vsrc[r], Vd + (r * 4 + wave) * 512);
-      }
-    } else {
-      // Tail tile: rows past the last key re-read the last key (finite
-      // data; those keys are masked).
-#pragma unroll
-      for (int r = 0; r < NCOPY; ++r) {
-        const int row = ((r * 4 + wave) * 64 + lane) / CPR;
-        const int key = min(t0 + row, p.Tk - 1);
-        copy16_to_lds(Kg + (size_t)key * D + (ksrc[r] - row * D), Kd + (r * 4 + wave) * 512);
-        copy16_to_lds(Vg + (size_t)key * D + (vsrc[r] - row * D), Vd + (r * 4 + wave) * 512);
-      }
+    for (int r = 0; r < NCOPY; ++r) {
+      copy16_buf_to_lds(krsrc, Kd + (r * NW + wave) * 512, ksrc[r], soff);
+      copy16_buf_to_lds(vrsrc, Vd + (r * NW + wave) * 512, vsrc[r], soff);
     }
   };
+  // Wait until the copies of tile t (issued `later` tiles before the newest
+  // ones) have landed: the vector-memory counter counts 2*NCOPY per tile.
+  auto wait_copies = [&](int later) {
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<4 * NCOPY>());
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NCOPY>());
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  };
 
-  // K operand read bases (stage 0, key block 0): stage S adds S*TILE and key
+  // K operand read bases (stage 0, key block 0): stage s adds s*TILE and key
   // block kb adds 32*kb*D elements.  k_swz of rows 32*kb + col is k_swz(col).
-  const bf16* kread[NC];
+  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
+  lds_bf16x8_t* kread[NC];
   {
     const int sw = k_swz<D>(col);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) kread[cc] = lds + col * D + (((2 * cc + half) ^ sw) << 3);
+    for (int cc = 0; cc < NC; ++cc)
+      kread[cc] = (lds_bf16x8_t*)(lds_char_t*)(lds + col * D + (((2 * cc + half) ^ sw) << 3));
   }
   // V operand bases for the transposing reads: input lane 4j + q of 16-lane
   // group G addresses 4 head-dim values starting at 32*db + 16*(G%2) + 4q
@@ -256,7 +285,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int dd = 32 * db + tr_d;
-      vread[db] = lds_addr(lds + 2 * TILE + r0 * D + (((dd >> 3) ^ sw) << 3) + (dd & 7));
+      vread[db] = lds_addr(lds + kStages * TILE + r0 * D + (((dd >> 3) ^ sw) << 3) + (dd & 7));
     }
   }
 
@@ -269,30 +298,25 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  auto step = [&](auto stage_c, int t) {
-    constexpr int S = decltype(stage_c)::value;
-    const int t0 = t * kBN;
-    if (t + 1 < ntiles) issue_copies(IC<1 - S>{}, t0 + kBN);
+  for (int t = 0; t < min(ntiles, kStages - 1); ++t) issue_copies(t);
 
-    // S^T for the tile's two 32-key blocks.  Under the causal mask a block
-    // whose first key lies after this wavefront's last row is all masked.
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * kBN;
+    wait_copies(min(ntiles - 1 - t, kStages - 2));
+    __syncthreads();   // tile t visible to all; stage (t-1) % kStages free
+    if (t + kStages - 1 < ntiles) issue_copies(t + kStages - 1);
+    const int st = t % kStages;
+
+    // S^T for the tile's two 32-key blocks (on the diagonal tile a block may
+    // be entirely masked; it is computed anyway and masked below).
     f32x16 s[2];
-    bool act[2];
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      act[kb] = !CAUSAL || (t0 + 32 * kb <= q0w + 31);
+      s[kb] = mma_32x32x16(kread[0][(st * TILE + kb * 32 * D) / 8], qf[0], f32x16{});
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      if (act[kb]) {
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          const bf16x8 a = *(const bf16x8*)(kread[cc] + S * TILE + kb * 32 * D);
-          s[kb] = mma_32x32x16(a, qf[cc], s[kb]);
-        }
-      }
+      for (int cc = 1; cc < NC; ++cc)
+        s[kb] = mma_32x32x16(kread[cc][(st * TILE + kb * 32 * D) / 8], qf[cc], s[kb]);
     }
-    __builtin_amdgcn_s_setprio(0);
 
     // Mask (only tiles that cross the diagonal or the key tail): -inf
     // before the max, so masked keys get probability exactly 0.
@@ -303,17 +327,17 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = act[kb] && key < p.Tk && (!CAUSAL || key <= my_q);
+          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q);
           s[kb][r] = vis ? s[kb][r] : kNegInf;
         }
     }
 
-    // Row max of the tile (in-lane, then across the two wave halves).
-    float mt = fmaxf(s[0][0], s[1][0]);
+    // Row max of the tile: a chain of 3-input maxima in-lane, then across
+    // the two wave halves.
+    float mt = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 15; r += 2)
-      mt = fmaxf(mt, fmaxf(fmaxf(s[0][r], s[0][r + 1]), fmaxf(s[1][r], s[1][r + 1])));
-    mt = fmaxf(mt, fmaxf(s[0][15], s[1][15]));
+    for (int i = 2; i < 32; i += 2)
+      mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
     mt = max_halves(mt);
 
     // Online update of the running max.  The accumulator is rescaled only
@@ -329,15 +353,15 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
     l *= corr;
     m = m_new;
     const float mc = m * c;
-    float ls = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mc));
-        ls += s[kb][r];
+        ls[r & 3] += s[kb][r];
       }
-    l += ls;
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
     // O^T += V^T P^T in four groups g = (kb, j2).  The B operand for keys
     // {16*j2 + 4*half + 0..3, 16*j2 + 8 + 4*half + 0..3} of block kb is
@@ -346,13 +370,16 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
     // The reads of group g+1 are in flight while group g multiplies.  A
     // block that is entirely masked has probabilities 0 and is multiplied
     // anyway (this happens only on the diagonal tile).
+    uint32_t vst[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) vst[db] = vread[db] + (uint32_t)(st * TILE * 2);
     auto issue_v = [&](auto g_c, u32x2 (&v)[ND][2]) {
       constexpr int G = decltype(g_c)::value;
-      constexpr int OFF = (S * TILE + (32 * (G >> 1) + 16 * (G & 1)) * D) * 2;
+      constexpr int OFF = (32 * (G >> 1) + 16 * (G & 1)) * D * 2;
       static_for<0, ND>([&](auto db_c) {
         constexpr int DB = decltype(db_c)::value;
-        v[DB][0] = lds_read_tr<OFF>(vread[DB]);
-        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vread[DB]);
+        v[DB][0] = lds_read_tr<OFF>(vst[DB]);
+        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vst[DB]);
       });
     };
     auto multiply = [&](auto g_c, u32x2 (&v)[ND][2]) {
@@ -378,7 +405,6 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
       u32x2 va[ND][2], vb[ND][2];
       issue_v(IC<0>{}, va);
       issue_v(IC<1>{}, vb);
-      __builtin_amdgcn_s_setprio(1);
       lds_tr_wait<NR>(va);
       multiply(IC<0>{}, va);
       issue_v(IC<2>{}, va);
@@ -389,19 +415,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(const FwdParams p
       multiply(IC<2>{}, va);
       lds_tr_wait<0>(vb);
       multiply(IC<3>{}, vb);
-      __builtin_amdgcn_s_setprio(0);
     }
-
-    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's copies of the next tile have landed
-    __syncthreads();
-  };
-
-  if (ntiles > 0) issue_copies(IC<0>{}, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
-    step(IC<0>{}, t);
-    if (t + 1 < ntiles) step(IC<1>{}, t + 1);
   }
 
   // Finalise: one division per row; lse in natural log.
@@ -553,14 +567,14 @@ hipError_t launch_bf16_hg(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;
   const int hg = (p.g % 4 == 0) ? 4 : (p.g % 2 == 0) ? 2 : 1;
   p.groups = p.g / hg;
-  const int bmpos = 128 / hg;
+  const int bmpos = 32 * (kFwdThreads / 64) / hg;
   dim3 grid((unsigned)(p.B * p.Hkv * p.groups), (unsigned)((p.Tq + bmpos - 1) / bmpos));
   if (hg == 4)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(kFwdThreads), 0, stream, p);
   else if (hg == 2)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(kFwdThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1>), grid, dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -119,6 +119,31 @@ def fa_release_workspace() -> None:
     load().fa_release_workspace()
 
 
+def prepared(entry: str, *args, stream=None):
+    """Marshal the arguments of entry point `entry` once and return a
+    zero-argument callable that makes the call (for timing loops: no
+    per-call pointer extraction).  The callable raises FAError on a
+    nonzero status."""
+    lib = load()
+    fn = getattr(lib, entry)
+    conv = []
+    for a, t in zip(args, fn.argtypes[:-1]):
+        if t is ctypes.c_void_p:
+            conv.append(_ptr(a))
+        elif t is ctypes.c_float:
+            conv.append(float(a))
+        else:
+            conv.append(int(a))
+    conv.append(_stream(stream))
+    cargs = [t(v) if v is not None else None for t, v in zip(fn.argtypes, conv)]
+
+    def call():
+        st = fn(*cargs)
+        if st != FA_OK:
+            raise FAError(st, entry)
+    return call
+
+
 # --- torch conveniences --------------------------------------------------------
 
 def _require(cond, msg):
