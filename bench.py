@@ -285,9 +285,9 @@ def main():
                           "traffic": measured_traffic(name)}
             log(f"[bench]   {also[name]}")
         wd = inputs.FLASH_DECODE
-        S = fa.fa_decode_splits(wd.B, wd.Hkv, wd.Tk_max, wd.d, args.decode_splits)
-        log(f"[bench] {wd.name}, num_splits {S}")
-        wl, ev, nbytes, ntok = decode_case(torch, fa, wd, 50, 5, args.decode_splits)
+        S = fa.fa_decode_workgroups(wd.B, wd.Hq, wd.Hkv, wd.Tk_max, wd.d, args.decode_splits)
+        log(f"[bench] {wd.name}, {S} key ranges")
+        wl, ev, nbytes, ntok = decode_case(torch, fa, wd, 200, 100, args.decode_splits)
         gbs = nbytes / (ev * 1e-3) / 1e9
         also["flash_decode"] = {"value": round(nbytes / wl / 1e9, 1), "unit": "GB/s",
                                 "us_per_call": round(wl * 1e6, 2), "call_us_events": round(ev * 1e3, 2),

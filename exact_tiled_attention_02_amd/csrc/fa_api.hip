@@ -70,23 +70,27 @@ fa::FwdParams make_fwd(const void* q, const void* k, const void* v, void* o, flo
   return p;
 }
 
-int auto_splits(int B, int Hkv, int Tk_max) {
-  // Enough workgroups to cover the 256 compute units several times over,
-  // with pieces of at least 256 keys.
-  const int64_t units = (int64_t)B * Hkv;
-  int64_t s = (2048 + units - 1) / units;
-  const int64_t cap = (Tk_max + 255) / 256;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return (int)s;
-}
+// Largest workgroup count accepted for a decode call.
+constexpr int kMaxDecodeWorkgroups = 1 << 20;
 
-int clamp_splits(int B, int Hkv, int Tk_max, int num_splits) {
-  int s = num_splits == 0 ? auto_splits(B, Hkv, Tk_max) : num_splits;
-  const int cap = (Tk_max + fa::kDecodeTile - 1) / fa::kDecodeTile;
-  if (s > cap) s = cap;
-  if (s < 1) s = 1;
-  return s;
+// Workgroups for a decode call: the caller's count, or (0) as many as the
+// device keeps resident at once, so that every workgroup starts at launch
+// and all of them finish together.  Cached per (device, d, heads per
+// workgroup).  Returns a negative status if the device cannot be queried.
+int decode_workgroups(int d, int hpw, int num_splits) {
+  if (num_splits > 0) return num_splits < kMaxDecodeWorkgroups ? num_splits : kMaxDecodeWorkgroups;
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -FA_ERR_DEVICE;
+  const std::pair<int, int> key(dev, d * 16 + hpw);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  const int w = fa::decode_resident_workgroups(d, hpw);
+  if (w <= 0) return -FA_ERR_DEVICE;
+  cache[key] = w;
+  return w;
 }
 
 }  // namespace
@@ -111,10 +115,11 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return map_err(fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
 }
 
-int fa_decode_splits(int B, int Hkv, int Tk_max, int d, int num_splits) {
-  (void)d;
-  if (B < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return 1;
-  return clamp_splits(B, Hkv, Tk_max, num_splits);
+int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0 || Hq % Hkv != 0)
+    return -FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return -FA_ERR_UNSUPPORTED;
+  return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), num_splits);
 }
 
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens, void* o,
@@ -125,17 +130,22 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   if (B == 0 || Hq == 0) return FA_OK;
   if (q == nullptr || o == nullptr || seqlens == nullptr) return FA_ERR_NULL;
   if (Tk_max > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_NULL;
-  // Sequences run along grid.z and kv heads along grid.y.
-  if (B > 65535 || Hkv > 65535 || (int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
+  // One merge wavefront per (sequence, query head).
+  if ((int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
 
-  const int S = clamp_splits(B, Hkv, Tk_max, num_splits);
-  const size_t nparts = (size_t)B * Hq * S;
-  const size_t need = nparts * (size_t)(d + 2) * sizeof(float);
+  const int g = Hq / Hkv;
+  const int hpw = fa::decode_heads_per_workgroup(g);
+  const int W = decode_workgroups(d, hpw, num_splits);
+  if (W < 0) return -W;
+  const size_t slots = fa::decode_slots(W, B, Hkv, g, hpw);
+  const size_t cum_bytes = (((size_t)B + 1) * sizeof(long long) + 255) / 256 * 256;
+  const size_t nparts = slots * hpw;
+  const size_t need = cum_bytes + nparts * (size_t)(d + 2) * sizeof(float);
   hipStream_t hs = (hipStream_t)stream;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
-  void* ws = nullptr;
+  char* ws = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[std::make_pair(dev, hs)];
@@ -145,14 +155,14 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
         w.ptr = nullptr;
         w.bytes = 0;
       }
-      size_t grow = need + need / 4;
+      const size_t grow = need + need / 4;
       if (hipMallocAsync(&w.ptr, grow, hs) != hipSuccess) {
         w.ptr = nullptr;
         return FA_ERR_ALLOC;
       }
       w.bytes = grow;
     }
-    ws = w.ptr;
+    ws = (char*)w.ptr;
   }
 
   fa::DecodeParams p{};
@@ -161,15 +171,17 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   p.vcache = vcache;
   p.seqlens = seqlens;
   p.o = o;
-  p.part_m = (float*)ws;
+  p.cum = (long long*)ws;
+  p.part_m = (float*)(ws + cum_bytes);
   p.part_l = p.part_m + nparts;
   p.part_o = p.part_l + nparts;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.Tk_max = Tk_max;
-  p.g = Hq / Hkv;
-  p.splits = S;
+  p.g = g;
+  p.hpw = hpw;
+  p.W = W;
   p.c = (float)(1.4426950408889634 / sqrt((double)d));
   return map_err(fa::launch_decode(p, d, hs));
 }

@@ -19,26 +19,51 @@ struct FwdParams {
 };
 
 // One decode call.  q,o: [B,Hq,d]; caches: [B,Hkv,Tk_max,d].
+//
+// The valid keys of all (sequence, kv head, head group) segments, laid end to
+// end in that order, form one key space of sum_b n_b * Hkv * groups keys.
+// Workgroup w takes the contiguous range [w * per, (w + 1) * per) of it and
+// writes one partial (m, l, o) for every segment the range touches, into slot
+// w + segment.  The merge kernel combines the slots of each segment.
 struct DecodeParams {
   const void* q;
   const void* kcache;
   const void* vcache;
   const int* seqlens;
   void* o;
-  float* part_m;   // [B, Hq, S] running max (base-2 scaled), -inf for empty pieces
-  float* part_l;   // [B, Hq, S] sum of 2^(s*c - m)
-  float* part_o;   // [B, Hq, S, d] unnormalised weighted value sums
+  long long* cum;  // [B + 1] exclusive prefix sums of the clamped sequence lengths
+  float* part_m;   // [slots, hpw] running max (base-2 scaled)
+  float* part_l;   // [slots, hpw] sum of 2^(s*c - m)
+  float* part_o;   // [slots, hpw, d] unnormalised weighted value sums
   int B, Hq, Hkv, Tk_max;
-  int g;
-  int splits;
+  int g;           // Hq / Hkv
+  int hpw;         // query heads per workgroup (a divisor of g)
+  int W;           // workgroups sharing the key space
   float c;         // log2(e) / sqrt(d)
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
+// Workgroups that the decode kernel for (d, hpw) keeps resident on the
+// current device at once; 0 if the device cannot be queried.
+int decode_resident_workgroups(int d, int hpw);
 
-// Key granularity of decode pieces: a piece covers a multiple of this many keys.
-constexpr int kDecodeTile = 64;
+// Query heads one decode workgroup serves (a divisor of the group size g).
+inline int decode_heads_per_workgroup(int g) {
+  return (g % 8 == 0) ? 8 : (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+}
+
+// Partial slots a decode call with W workgroups needs.
+inline size_t decode_slots(int W, int B, int Hkv, int g, int hpw) {
+  return (size_t)W + (size_t)B * Hkv * (g / hpw);
+}
+
+// Keys per workgroup range: ceil(total / W) rounded up to 16.  The decode
+// and merge kernels both evaluate exactly this.
+__host__ __device__ inline long long decode_range(long long total, int W) {
+  const long long per = (total + W - 1) / W;
+  return ((per + 15) / 16) * 16;
+}
 
 }  // namespace fa

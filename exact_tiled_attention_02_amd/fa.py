@@ -1,6 +1,6 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_decode``, ``fa_decode_splits``,
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_decode``, ``fa_decode_workgroups``,
 ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
 with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
                 4: "FA_ERR_ALLOC", 5: "FA_ERR_LAUNCH", 6: "FA_ERR_DEVICE"}
+STATUS_CODES = {v: k for k, v in STATUS_NAMES.items()}
 
 _lib = None
 _lock = threading.Lock()
@@ -53,8 +54,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd_f32.restype = I
         lib.fa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         lib.fa_decode.restype = I
-        lib.fa_decode_splits.argtypes = [I, I, I, I, I]
-        lib.fa_decode_splits.restype = I
+        lib.fa_decode_workgroups.argtypes = [I, I, I, I, I, I]
+        lib.fa_decode_workgroups.restype = I
         lib.fa_strerror.argtypes = [I]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_release_workspace.argtypes = []
@@ -107,8 +108,12 @@ def fa_decode(q, kcache, vcache, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits, 
                             Hkv, Tk_max, d, int(num_splits), _stream(stream)), "fa_decode")
 
 
-def fa_decode_splits(B, Hkv, Tk_max, d, num_splits) -> int:
-    return load().fa_decode_splits(B, Hkv, Tk_max, d, int(num_splits))
+def fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
+    """Workgroup count fa_decode would use; raises FAError on a negative status."""
+    n = load().fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, int(num_splits))
+    if n < 0:
+        raise FAError(-n, "fa_decode_workgroups")
+    return n
 
 
 def fa_strerror(status: int) -> str:

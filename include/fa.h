@@ -93,10 +93,14 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 /*
  * fa_decode -- single-query attention over a KV cache with split-KV
  * flash-decoding ([NOTE] section "Prefill i dekodowanie to różne problemy",
- * Flash-decoding paragraph): each sequence's valid keys are cut into
- * num_splits contiguous pieces, every piece yields a partial (m, l, o) for
- * the whole query-head group of its kv head, and a second kernel merges the
- * partials with the rescaling rule of [BOOK5] section 5.3.3 (Example 5-6).
+ * Flash-decoding paragraph).  The valid keys of every (sequence, kv head)
+ * are laid end to end in one key space, which is cut into num_splits
+ * contiguous ranges of equal length, one per workgroup, so every workgroup
+ * streams the same number of cache bytes whatever the mix of sequence
+ * lengths.  A range yields a partial (m, l, o) for the query-head group of
+ * each kv head it touches, and a second kernel merges the partials of each
+ * (sequence, query head) with the rescaling rule of [BOOK5] section 5.3.3
+ * (Example 5-6).
  *
  *   q       : [B, Hq, d] bf16 (one query token per sequence)
  *   kcache  : [B, Hkv, Tk_max, d] bf16      vcache : same shape
@@ -105,29 +109,34 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *             device; slots at or beyond seqlens[b] are never read.
  *   o       : [B, Hq, d] bf16; a sequence with seqlens[b] == 0 gets o = 0.
  *   scale is fixed at 1/sqrt(d).
- *   num_splits: pieces per sequence.  0 lets the library choose from the
- *             shape; a positive request is clamped to ceil(Tk_max / 64).
- *             The result does not depend on the split count beyond
- *             floating-point rounding, and for a fixed split count it is
- *             bitwise reproducible (the merge runs in a fixed order,
- *             [BOOK5] section 5.2.4 on split reductions and determinism).
+ *   num_splits: number of key ranges (workgroups).  0 lets the library use
+ *             as many as the device keeps resident at once; a positive
+ *             request is capped at 2^20.  The result does not depend on the
+ *             split count beyond floating-point rounding, and for a fixed
+ *             split count it is bitwise reproducible (the merge runs in a
+ *             fixed order, [BOOK5] section 5.2.4 on split reductions and
+ *             determinism).
  *
- * Workspace: the partials, B*Hq*splits*(d+2) fp32 values, live in a buffer
- * the library owns per (device, stream), grown on demand with stream-ordered
- * allocation on `stream` and kept for reuse.  Concurrent calls on the same
- * stream are ordered by the stream; calls on different streams use
- * different buffers.  fa_release_workspace() frees them.
+ * Workspace: the prefix sums of the sequence lengths ((B+1) int64) and the
+ * partials ((num_splits + B*Hkv*(g/h)) * h * (d+2) fp32 values, h the query
+ * heads one workgroup serves, g = Hq/Hkv) live in a buffer the library owns
+ * per (device, stream), grown on demand with stream-ordered allocation on
+ * `stream` and kept for reuse.  Concurrent calls on the same stream are
+ * ordered by the stream; calls on different streams use different buffers.
+ * fa_release_workspace() frees them.
  * Errors: FA_ERR_NULL, FA_ERR_SHAPE (negative sizes, Hq % Hkv != 0,
  * num_splits < 0), FA_ERR_UNSUPPORTED (d not 64/128), FA_ERR_ALLOC,
- * FA_ERR_LAUNCH.
+ * FA_ERR_LAUNCH, FA_ERR_DEVICE (num_splits == 0 and the current device
+ * cannot be queried).
  */
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens,
               void* o, int B, int Hq, int Hkv, int Tk_max, int d, int num_splits,
               void* stream);
 
-/* The split count fa_decode uses for a request (after the 0 = automatic
- * choice and the clamp), without launching anything. */
-int fa_decode_splits(int B, int Hkv, int Tk_max, int d, int num_splits);
+/* The number of key ranges (workgroups) fa_decode uses for a request, after
+ * the 0 = automatic choice (which needs a current HIP device) and the cap,
+ * without launching anything.  Returns minus the status code on error. */
+int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
 
 /* Static description of a status code (never NULL). */
 const char* fa_strerror(int status);

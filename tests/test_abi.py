@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_strerror", "fa_release_workspace",
-              "fa_decode_splits"):
+              "fa_decode_workgroups"):
         assert n in names
 
 
@@ -76,20 +76,23 @@ def test_fwd_validation(lib, entry, args, status):
     ((FAKE, P, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, 4), 1),          # kcache NULL
     ((P, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, 4), 1),
     ((P, P, P, P, P, 0, 8, 2, 64, 128, 4), 0),                      # empty batch
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, 70000, 8, 2, 64, 128, 4), 2),   # B beyond grid.z
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 28, 8, 2, 64, 128, 4), 2), # B*Hq merge grid overflow
 ])
 def test_decode_validation(lib, args, status):
     assert lib.fa_decode(*args, None) == status
 
 
-def test_decode_split_planning(lib):
-    # Automatic choice for the 16-sequence, 8-kv-head cache of 32768 slots.
-    s = fa.fa_decode_splits(16, 8, 32768, 128, 0)
-    assert 1 <= s <= 32768 // 64
-    assert fa.fa_decode_splits(16, 8, 32768, 128, 16) == 16
-    assert fa.fa_decode_splits(16, 8, 32768, 128, 10**6) == 32768 // 64   # clamp
-    assert fa.fa_decode_splits(1, 1, 100, 128, 7) == 2                   # ceil(100/64)
-    assert fa.fa_decode_splits(1, 1, 0, 128, 7) == 1
+def test_decode_workgroup_planning(lib):
+    # An explicit count is used as given, capped at 2^20; bad shapes give
+    # minus the status code.  (The automatic choice needs a device and is
+    # covered by the GPU tests.)
+    assert lib.fa_decode_workgroups(16, 32, 8, 32768, 128, 16) == 16
+    assert lib.fa_decode_workgroups(16, 32, 8, 32768, 128, 7) == 7
+    assert lib.fa_decode_workgroups(16, 32, 8, 32768, 128, 1 << 30) == 1 << 20
+    assert lib.fa_decode_workgroups(1, 1, 1, 0, 64, 3) == 3
+    assert lib.fa_decode_workgroups(16, 30, 8, 32768, 128, 16) == -fa.STATUS_CODES["FA_ERR_SHAPE"]
+    assert lib.fa_decode_workgroups(16, 32, 8, 32768, 96, 16) == -fa.STATUS_CODES["FA_ERR_UNSUPPORTED"]
+    assert lib.fa_decode_workgroups(16, 32, 8, 32768, 128, -1) == -fa.STATUS_CODES["FA_ERR_SHAPE"]
 
 
 def test_strerror(lib):

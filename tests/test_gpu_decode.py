@@ -110,3 +110,26 @@ def test_decode_equals_single_row_forward():
         fa.fa_fwd(tq, tk, tv, o, None, 1, 8, 2, 1, n, 128, False, 1 / math.sqrt(128))
         torch.cuda.synchronize()
         check("O", O[b], host_bf16_as_f64(o)[0, :, 0], BF16_O_TOL)
+
+
+def test_automatic_workgroup_count_fills_the_device():
+    from exact_tiled_attention_02_amd import fa
+    w = inputs.FLASH_DECODE
+    n = fa.fa_decode_workgroups(w.B, w.Hq, w.Hkv, w.Tk_max, w.d, 0)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say("auto workgroups", n, "CUs", cus)
+    assert n >= cus and n % cus == 0
+
+
+@pytest.mark.parametrize("num_splits", [700, 4096])
+def test_decode_many_ranges_per_sequence(num_splits):
+    """More than 64 key ranges (workgroups) land on one sequence, so the merge
+    combines its partials over several passes; most workgroups of the 4096
+    have no keys at all."""
+    w = inputs.Decode("t", B=2, Hq=4, Hkv=1, Tk_max=3000, d=128, seq_lo=1, seq_hi=3000, seed=24)
+    q, kc, vc, _ = inputs.decode_inputs(w)
+    sl = np.array([3000, 1234], np.int32)
+    say("fa_decode many ranges", num_splits)
+    O = run_decode(q, kc, vc, sl, num_splits)
+    Or, _ = oracle.decode_attention(q, kc, vc, sl)
+    check("O", O, Or, BF16_O_TOL)
