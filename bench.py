@@ -36,35 +36,48 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["exact_tiled_attention_02_amd/csrc/fa_fwd.hip",
-                  "exact_tiled_attention_02_amd/csrc/fa_decode.hip",
-                  "exact_tiled_attention_02_amd/csrc/fa_device.h"]
+# Sources each workload's kernels are built from: a traffic figure counts
+# only while they are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "prefill": ["exact_tiled_attention_02_amd/csrc/fa_fwd.hip",
+                "exact_tiled_attention_02_amd/csrc/fa_device.h",
+                "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
+    "decode": ["exact_tiled_attention_02_amd/csrc/fa_decode.hip",
+               "exact_tiled_attention_02_amd/csrc/fa_device.h",
+               "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernels changed since the counters were taken."""
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter summary (FETCH_SIZE and WRITE_SIZE scaled by what they
+    read for a copy of known size), or None when the kernel sources changed
+    since the counters were taken."""
     try:
         with open(TRAFFIC_FILE, encoding="utf-8") as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
     w = t.get("workloads", {}).get(workload)
-    return None if w is None else w.get("hbm_bytes_per_launch")
+    if w is None:
+        return None
+    from exact_tiled_attention_02_amd import inputs
+    kind = "decode" if isinstance(inputs.WORKLOADS[workload], inputs.Decode) else "prefill"
+    if w.get("kernel_source_hash") != kernel_source_hash(kind):
+        return None
+    return w.get("hbm_bytes_per_launch")
 
 
 # ----------------------------------------------------------------------------
