@@ -17,11 +17,12 @@
 // probabilities ever leave the chip.
 //
 // Mapping onto CDNA4:
-//  * 256 threads = 4 wavefronts; each wavefront owns 32 query rows of one
-//    query head.  A workgroup holds HG query heads of one grouped-query
-//    group (HG = 4, 2 or 1) so every K/V tile staged in LDS serves all of
-//    them ([NOTE] "Prefill i dekodowanie to różne problemy": GQA reuses
-//    each K/V tile g times).
+//  * The bf16 kernel's workgroup is 512 threads = 8 wavefronts, two per
+//    SIMD; each wavefront owns 32 query rows of one query head.  A
+//    workgroup holds HG query heads of one grouped-query group (HG = 4, 2
+//    or 1) so every K/V tile staged in LDS serves all of them ([NOTE]
+//    "Prefill i dekodowanie to różne problemy": GQA reuses each K/V tile g
+//    times).
 //  * Scores are computed transposed, S^T = K Q^T, with the 32x32x16 bf16
 //    matrix instruction: every lane then holds one query row's scores for 16
 //    keys, so the row max and row sum are in-lane reductions plus one
@@ -30,13 +31,14 @@
 //    the lane's own value and the probabilities feed the next matrix
 //    instruction straight from the score registers (a consistent permutation
 //    of the reduction index; no LDS round trip).
-//  * K tiles are stored row-major in LDS with XOR-swizzled 16-byte chunks;
-//    V tiles are stored transposed (V^T, head-dim rows, key columns) with
-//    XOR-swizzled 8-byte slots, so both operand reads avoid bank conflicts
-//    ([BOOK5] section 5.2.3 on spreading simultaneous requests over banks).
-//  * Two LDS stages: tile t+1 is fetched into registers while tile t is
-//    computed, then written to the other stage ([BOOK5] section 5.3.2,
-//    double buffering, Example 5-5).
+//  * K and V tiles are copied from HBM straight into LDS (buffer-resource
+//    loads with an LDS destination; keys past the end read as zeros) into
+//    four stages, the copy of tile t+3 being issued while tile t is
+//    computed ([BOOK5] section 5.3.2, double buffering, Example 5-5).  Both
+//    tiles are row-major with XOR-swizzled chunks: K is read 16 bytes per
+//    lane, V through the transposing LDS read, and neither read has bank
+//    conflicts ([BOOK5] section 5.2.3 on spreading simultaneous requests
+//    over banks).
 //  * Causal: key tiles starting after the workgroup's last row are never
 //    visited; only tiles crossing the diagonal (or the key tail) are masked,
 //    with -inf before the max ([FUSED07] task 07.2 pitfalls).  Workgroups
