@@ -151,6 +151,16 @@ constexpr int vmcnt_imm() {
   return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// Workgroup barrier of the tile loop.  __syncthreads() would also wait for
+// every global->LDS copy still in flight (its release fence covers them),
+// which would cap the copy lead at one tile; here each wavefront first waits
+// for the copies it needs (vmcnt) and for its own LDS reads, then meets the
+// others.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float max_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -305,7 +315,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = t * kBN;
     wait_copies(min(ntiles - 1 - t, kStages - 2));
-    __syncthreads();   // tile t visible to all; stage (t-1) % kStages free
+    tile_barrier();   // tile t visible to all; stage (t-1) % kStages free
     if (t + kStages - 1 < ntiles) issue_copies(t + kStages - 1);
     const int st = t % kStages;
 
