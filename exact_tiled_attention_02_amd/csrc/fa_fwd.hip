@@ -41,8 +41,9 @@
 //    over banks).
 //  * Causal: key tiles starting after the workgroup's last row are never
 //    visited; only tiles crossing the diagonal (or the key tail) are masked,
-//    with -inf before the max ([FUSED07] task 07.2 pitfalls).  Workgroups
-//    are issued heaviest query tile first.
+//    with -inf before the max ([FUSED07] task 07.2 pitfalls).  A workgroup
+//    pairs a light and the mirrored heavy half-tile of query rows so that
+//    all workgroups carry the same work.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -204,10 +205,30 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   x /= p.groups;
   const int kvh = x % p.Hkv;
   const int b = x / p.Hkv;
-  const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int q0 = qt * BMPOS;
   const int hq = kvh * p.g + grp * HG + wave / WPH;
-  const int q0w = q0 + (wave % WPH) * 32;
+  // Rows of this wavefront: q0w .. q0w + 31.  When the grid is too small to
+  // even out causal work by itself (p.pair), a workgroup owns, per query
+  // head, two half-tiles of BMPOS/2 rows: light half-tile i (few visible
+  // keys) and the mirrored heavy half-tile nh-1-i, so every workgroup
+  // carries the same work; the two wavefronts that share a SIMD (w and w+4)
+  // always get one light and one heavy block.
+  int q0w, q_end;      // q_end: one past the workgroup's last row
+  bool active = true;  // false for the second copy of a middle half-tile
+  if (CAUSAL && p.pair) {
+    constexpr int HALF = BMPOS / 2;
+    const int nh = (p.Tq + HALF - 1) / HALF;
+    const int i = blockIdx.y;
+    const int hh = wave % WPH;
+    const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
+    const int ht = heavy ? nh - 1 - i : i;
+    active = !(heavy && ht == i);
+    q0w = ht * HALF + (hh % (WPH / 2)) * 32;
+    q_end = min(p.Tq, (nh - i) * HALF);
+  } else {   // causal without pairing: heaviest query tile first
+    const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    q0w = qt * BMPOS + (wave % WPH) * 32;
+    q_end = min(p.Tq, (qt + 1) * BMPOS);
+  }
   const int my_q = q0w + col;
 
   const bf16* Qg = (const bf16*)p.q + (size_t)(b * p.Hq + hq) * p.Tq * D;
@@ -230,9 +251,10 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
   // Keys this workgroup needs: all, or under the causal mask those at or
   // before its last (real) query row.
-  const int q_last = min(p.Tq, q0 + BMPOS);
-  const int kend = CAUSAL ? min(p.Tk, q_last) : p.Tk;
+  const int kend = CAUSAL ? min(p.Tk, q_end) : p.Tk;
   const int ntiles = (kend + kBN - 1) / kBN;
+  // Last key tile this wavefront computes (its rows see no key after it).
+  const int my_tiles = !active ? 0 : CAUSAL ? min(ntiles, (q0w + 31) / kBN + 1) : ntiles;
 
   // Global->LDS copies through buffer resources covering this head's K and
   // V: reads past the last key return zeros (finite; those keys are masked).
@@ -317,6 +339,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     wait_copies(min(ntiles - 1 - t, kStages - 2));
     tile_barrier();   // tile t visible to all; stage (t-1) % kStages free
     if (t + kStages - 1 < ntiles) issue_copies(t + kStages - 1);
+    if (t >= my_tiles) continue;   // still copies and meets the barriers
     const int st = t % kStages;
 
     // S^T for the tile's two 32-key blocks (on the diagonal tile a block may
@@ -433,7 +456,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   // Finalise: one division per row; lse in natural log.
   const float lt = sum_halves(l);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (my_q < p.Tq) {
+  if (active && my_q < p.Tq) {
     bf16* Og = (bf16*)p.o + ((size_t)(b * p.Hq + hq) * p.Tq + my_q) * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -574,13 +597,40 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
   }
 }
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_hg(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;
   const int hg = (p.g % 4 == 0) ? 4 : (p.g % 2 == 0) ? 2 : 1;
   p.groups = p.g / hg;
   const int bmpos = 32 * (kFwdThreads / 64) / hg;
-  dim3 grid((unsigned)(p.B * p.Hkv * p.groups), (unsigned)((p.Tq + bmpos - 1) / bmpos));
+  const int nx = p.B * p.Hkv * p.groups;
+  int ny = (p.Tq + bmpos - 1) / bmpos;
+  // Causal work per query tile grows with its position.  With many
+  // workgroups per compute unit the hardware dispatcher evens that out
+  // (heaviest first); with fewer, each workgroup takes a light and the
+  // mirrored heavy half-tile instead.
+  p.pair = 0;
+  if (CAUSAL && (long long)nx * ny < 4LL * compute_units()) {
+    const int half = bmpos / 2;
+    ny = ((p.Tq + half - 1) / half + 1) / 2;
+    p.pair = 1;
+  }
+  dim3 grid((unsigned)nx, (unsigned)ny);
   if (hg == 4)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(kFwdThreads), 0, stream, p);
   else if (hg == 2)

@@ -16,6 +16,7 @@ struct FwdParams {
   int groups;      // g / hg: workgroups that share one kv head along x
   float c;         // |scale| * log2(e), the factor that turns scores into base-2 exponents
   int negate_q;    // scale < 0: queries are sign-flipped on load, c uses |scale|
+  int pair;        // causal: workgroups pair mirrored light/heavy half-tiles
 };
 
 // One decode call.  q,o: [B,Hq,d]; caches: [B,Hkv,Tk_max,d].
