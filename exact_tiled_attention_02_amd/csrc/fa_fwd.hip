@@ -127,6 +127,22 @@ __device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
   return r;
 }
 
+// 16-byte LDS read at addr + OFF bytes, issued as inline assembly so that
+// its place in the instruction stream (how far ahead of its use) is fixed
+// here rather than by the scheduler; not usable before lds_wait_tie().
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+// Wait until at most N LDS reads of this wavefront are outstanding, tied to
+// the operand that needed the wait.
+template <int N>
+__device__ __forceinline__ void lds_wait_tie(bf16x8& v) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 // Wait until at most N LDS reads of this wavefront are outstanding (they
 // complete in issue order); the operand group passed in is tied to the wait
 // so its uses cannot be scheduled before it.
@@ -298,13 +314,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
   // K operand read bases (stage 0, key block 0): stage s adds s*TILE and key
   // block kb adds 32*kb*D elements.  k_swz of rows 32*kb + col is k_swz(col).
-  typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_t;
-  lds_bf16x8_t* kread[NC];
+  uint32_t kread[NC];
   {
     const int sw = k_swz<D>(col);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc)
-      kread[cc] = (lds_bf16x8_t*)(lds_char_t*)(lds + col * D + (((2 * cc + half) ^ sw) << 3));
+    for (int cc = 0; cc < NC; ++cc) kread[cc] = lds_addr(lds + col * D + (((2 * cc + half) ^ sw) << 3));
   }
   // V operand bases for the transposing reads: input lane 4j + q of 16-lane
   // group G addresses 4 head-dim values starting at 32*db + 16*(G%2) + 4q
@@ -334,23 +348,38 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
   for (int t = 0; t < min(ntiles, kStages - 1); ++t) issue_copies(t);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile; ST = t % kStages is a compile-time constant, so every LDS
+  // operand address is a per-lane base plus an immediate offset.
+  auto tile = [&](int t, auto st_c) {
+    constexpr int ST = decltype(st_c)::value;
     const int t0 = t * kBN;
     wait_copies(min(ntiles - 1 - t, kStages - 2));
     tile_barrier();   // tile t visible to all; stage (t-1) % kStages free
     if (t + kStages - 1 < ntiles) issue_copies(t + kStages - 1);
-    if (t >= my_tiles) continue;   // still copies and meets the barriers
-    const int st = t % kStages;
+    if (t >= my_tiles) return;   // still copies and meets the barriers
 
     // S^T for the tile's two 32-key blocks (on the diagonal tile a block may
-    // be entirely masked; it is computed anyway and masked below).
+    // be entirely masked; it is computed anyway and masked below).  K
+    // operand I = 2*cc + kb is read PF operands ahead of its instruction;
+    // the two key blocks alternate so that consecutive instructions are
+    // independent.
     f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = mma_32x32x16(kread[0][(st * TILE + kb * 32 * D) / 8], qf[0], f32x16{});
-#pragma unroll
-      for (int cc = 1; cc < NC; ++cc)
-        s[kb] = mma_32x32x16(kread[cc][(st * TILE + kb * 32 * D) / 8], qf[cc], s[kb]);
+    {
+      constexpr int NF = 2 * NC;
+      constexpr int PF = NF < 8 ? NF : 8;
+      bf16x8 kf[NF];
+      auto read_k = [&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        kf[I] = lds_read_b128<(ST * TILE + (I & 1) * 32 * D) * 2>(kread[I >> 1]);
+      };
+      static_for<0, PF>(read_k);
+      static_for<0, NF>([&](auto i_c) {
+        constexpr int I = decltype(i_c)::value;
+        constexpr int AFTER = I + PF <= NF ? PF - 1 : NF - 1 - I;
+        lds_wait_tie<AFTER>(kf[I]);
+        s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? f32x16{} : s[I & 1]);
+        if constexpr (I + PF < NF) read_k(IC<I + PF>{});
+      });
     }
 
     // Mask (only tiles that cross the diagonal or the key tail): -inf
@@ -405,16 +434,13 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     // The reads of group g+1 are in flight while group g multiplies.  A
     // block that is entirely masked has probabilities 0 and is multiplied
     // anyway (this happens only on the diagonal tile).
-    uint32_t vst[ND];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) vst[db] = vread[db] + (uint32_t)(st * TILE * 2);
     auto issue_v = [&](auto g_c, u32x2 (&v)[ND][2]) {
       constexpr int G = decltype(g_c)::value;
-      constexpr int OFF = (32 * (G >> 1) + 16 * (G & 1)) * D * 2;
+      constexpr int OFF = (ST * TILE + (32 * (G >> 1) + 16 * (G & 1)) * D) * 2;
       static_for<0, ND>([&](auto db_c) {
         constexpr int DB = decltype(db_c)::value;
-        v[DB][0] = lds_read_tr<OFF>(vst[DB]);
-        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vst[DB]);
+        v[DB][0] = lds_read_tr<OFF>(vread[DB]);
+        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vread[DB]);
       });
     };
     auto multiply = [&](auto g_c, u32x2 (&v)[ND][2]) {
@@ -451,6 +477,12 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       lds_tr_wait<0>(vb);
       multiply(IC<3>{}, vb);
     }
+  };
+  for (int t = 0; t < ntiles; t += kStages) {
+    tile(t, IC<0>{});
+    if (t + 1 < ntiles) tile(t + 1, IC<1>{});
+    if (t + 2 < ntiles) tile(t + 2, IC<2>{});
+    if (t + 3 < ntiles) tile(t + 3, IC<3>{});
   }
 
   // Finalise: one division per row; lse in natural log.
