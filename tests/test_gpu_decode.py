@@ -133,3 +133,18 @@ def test_decode_many_ranges_per_sequence(num_splits):
     O = run_decode(q, kc, vc, sl, num_splits)
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
     check("O", O, Or, BF16_O_TOL)
+
+
+def test_workspace_reuse_across_shapes():
+    """Alternating batch sizes on one stream: the per-segment counters that
+    the last range of a segment uses to merge must start from zero whether
+    the library's workspace grew, shrank or was reused."""
+    cases = [(2, 40), (12, 300), (3, 1000), (12, 300), (2, 40)]
+    for i, (B, Tmax) in enumerate(cases):
+        w = inputs.Decode("t", B=B, Hq=8, Hkv=2, Tk_max=Tmax, d=128, seq_lo=1, seq_hi=Tmax,
+                          seed=30 + i)
+        q, kc, vc, sl = inputs.decode_inputs(w)
+        say("fa_decode reuse", B, Tmax)
+        O = run_decode(q, kc, vc, sl, 0 if i % 2 else 37)
+        Or, _ = oracle.decode_attention(q, kc, vc, sl)
+        check("O", O, Or, BF16_O_TOL)
