@@ -61,4 +61,38 @@ __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) const char lds_char_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_char_t*)p;
+}
+
+// Copy 16 bytes per lane from a buffer resource (byte offset voff + soff;
+// past the resource's size the data read is zero) straight into LDS at
+// lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void copy16_buf_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
+                                                  uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate that waits for the vector-memory counter to drop to N
+// and leaves the other counters unconstrained.
+template <int N>
+constexpr int vmcnt_imm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+// Workgroup barrier of the tile loop.  __syncthreads() would also wait for
+// every global->LDS copy still in flight (its release fence covers them),
+// which would cap the copy lead at one tile; here each wavefront first waits
+// for the copies it needs (vmcnt) and for its own LDS reads, then meets the
+// others.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace fa
