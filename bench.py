@@ -162,6 +162,25 @@ def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
     return wall, ev_ms, kv_bytes + io_bytes, int(seqlens.sum())
 
 
+def read_ceiling(torch, fa, nbytes=1 << 30, copies=2, steps=50, warmup=10):
+    """Achievable read bandwidth of the device: the library's read probe
+    streaming `nbytes` once per call (buffers used in rotation), GB/s."""
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    calls = [fa.prepared("fa_read_probe", b, nbytes, sink, stream=stream) for b in bufs]
+    it = [0]
+
+    def launch():
+        calls[it[0] % copies]()
+        it[0] += 1
+
+    _, ev_ms = time_calls(torch, launch, steps, warmup)
+    del bufs
+    torch.cuda.empty_cache()
+    return nbytes / (ev_ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, budget_s=12.0, max_s=30.0):
     """Time the fp64 oracle on whole (batch, head) pairs of the workload until
     about `budget_s` seconds of CPU work, and scale to TFLOP/s."""
@@ -302,7 +321,11 @@ def main():
         log(f"[bench] {wd.name}, {S} key ranges")
         wl, ev, nbytes, ntok = decode_case(torch, fa, wd, 200, 100, args.decode_splits)
         gbs = nbytes / (ev * 1e-3) / 1e9
+        ceil_gbs = read_ceiling(torch, fa)
+        log(f"[bench] read probe (1 GiB streamed once): {ceil_gbs:.1f} GB/s")
         also["flash_decode"] = {"value": round(nbytes / wl / 1e9, 1), "unit": "GB/s",
+                                "read_probe_gbs": round(ceil_gbs, 1),
+                                "frac_of_read_probe": round(gbs / ceil_gbs, 4),
                                 "us_per_call": round(wl * 1e6, 2), "call_us_events": round(ev * 1e3, 2),
                                 "num_splits": S, "algorithmic_bytes": nbytes, "kv_tokens": ntok,
                                 "roofline": {"bound": "hbm", "achieved": round(gbs, 1),

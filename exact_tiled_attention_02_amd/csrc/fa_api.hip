@@ -186,6 +186,13 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   return map_err(fa::launch_decode(p, d, hs));
 }
 
+int fa_read_probe(const void* src, size_t bytes, unsigned* sink, void* stream) {
+  if (bytes % 16 != 0 || bytes / ((size_t)1 << 20) >= (size_t)INT32_MAX) return FA_ERR_SHAPE;
+  if (bytes == 0) return FA_OK;
+  if (src == nullptr || sink == nullptr) return FA_ERR_NULL;
+  return map_err(fa::launch_read_probe(src, bytes, sink, (hipStream_t)stream));
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "success";

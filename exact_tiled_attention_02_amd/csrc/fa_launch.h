@@ -49,6 +49,9 @@ hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 // Workgroups that the decode kernel for (d, hpw) keeps resident on the
 // current device at once; 0 if the device cannot be queried.
 int decode_resident_workgroups(int d, int hpw);
+// Streams `bytes` (a multiple of 16) from src once, XOR-folding them into
+// *sink (which the caller zeroes).
+hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t stream);
 
 // Query heads one decode workgroup serves (a divisor of the group size g).
 inline int decode_heads_per_workgroup(int g) {

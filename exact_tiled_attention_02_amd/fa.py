@@ -1,7 +1,7 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
 The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_decode``, ``fa_decode_workgroups``,
-``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
+``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
 with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
 default stream) or objects with a ``cuda_stream`` attribute.  A nonzero
@@ -58,6 +58,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode_workgroups.restype = I
         lib.fa_strerror.argtypes = [I]
         lib.fa_strerror.restype = ctypes.c_char_p
+        lib.fa_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+        lib.fa_read_probe.restype = I
         lib.fa_release_workspace.argtypes = []
         lib.fa_release_workspace.restype = None
         _lib = lib
@@ -114,6 +116,10 @@ def fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
     if n < 0:
         raise FAError(-n, "fa_decode_workgroups")
     return n
+
+
+def fa_read_probe(src, nbytes, sink, stream=None) -> None:
+    _check(load().fa_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)), "fa_read_probe")
 
 
 def fa_strerror(status: int) -> str:

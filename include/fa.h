@@ -33,6 +33,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -137,6 +139,20 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
  * the 0 = automatic choice (which needs a current HIP device) and the cap,
  * without launching anything.  Returns minus the status code on error. */
 int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
+
+/*
+ * fa_read_probe -- measurement utility, not part of the attention path:
+ * reads `bytes` bytes of device memory at `src` exactly once with 16-byte
+ * loads (one 1 MiB chunk per workgroup, several loads in flight per lane)
+ * and XORs every 32-bit word into *sink (device memory, zeroed by the
+ * caller), so that a caller can time the device's achievable read
+ * bandwidth and report it beside fa_decode's, whose workload is a single
+ * stream over the KV cache ([NOTE] "Prefill i dekodowanie to różne
+ * problemy": decode runs at memory speed).  Enqueued on `stream`.
+ * Errors: FA_ERR_SHAPE (bytes not a multiple of 16), FA_ERR_NULL,
+ * FA_ERR_LAUNCH.  bytes == 0 is a no-op.
+ */
+int fa_read_probe(const void* src, size_t bytes, unsigned* sink, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_strerror", "fa_release_workspace",
-              "fa_decode_workgroups"):
+              "fa_decode_workgroups", "fa_read_probe"):
         assert n in names
 
 
@@ -93,6 +93,14 @@ def test_decode_workgroup_planning(lib):
     assert lib.fa_decode_workgroups(16, 30, 8, 32768, 128, 16) == -fa.STATUS_CODES["FA_ERR_SHAPE"]
     assert lib.fa_decode_workgroups(16, 32, 8, 32768, 96, 16) == -fa.STATUS_CODES["FA_ERR_UNSUPPORTED"]
     assert lib.fa_decode_workgroups(16, 32, 8, 32768, 128, -1) == -fa.STATUS_CODES["FA_ERR_SHAPE"]
+
+
+def test_read_probe_validation(lib):
+    # (src, bytes, sink): checked before any launch.
+    assert lib.fa_read_probe(FAKE, 17, FAKE, None) == fa.STATUS_CODES["FA_ERR_SHAPE"]
+    assert lib.fa_read_probe(None, 1024, FAKE, None) == fa.STATUS_CODES["FA_ERR_NULL"]
+    assert lib.fa_read_probe(FAKE, 1024, None, None) == fa.STATUS_CODES["FA_ERR_NULL"]
+    assert lib.fa_read_probe(None, 0, None, None) == fa.STATUS_CODES["FA_OK"]
 
 
 def test_strerror(lib):

@@ -148,3 +148,19 @@ def test_workspace_reuse_across_shapes():
         O = run_decode(q, kc, vc, sl, 0 if i % 2 else 37)
         Or, _ = oracle.decode_attention(q, kc, vc, sl)
         check("O", O, Or, BF16_O_TOL)
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, 3 * (1 << 20)])
+def test_read_probe_checksum(nbytes):
+    """The read probe touches every word exactly once: its XOR checksum
+    equals numpy's over the same bytes."""
+    from exact_tiled_attention_02_amd import fa
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("fa_read_probe", nbytes)
+    fa.fa_read_probe(src, nbytes, sink, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host) if host.size else np.uint32(0)
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(want)
