@@ -21,6 +21,7 @@ from .attention import (  # noqa: F401
     softmax_attention,
     softmax_attention_rows,
     online_fold_attention,
+    attention_backward,
     decode_attention,
     decode_split_merge,
     online_normalizer,

@@ -147,6 +147,57 @@ def softmax_attention_rows(q, k, v, *, causal: bool, scale: float, b: int, h: in
 
 
 # --------------------------------------------------------------------------
+# Backward pass: gradients of O with respect to q, k, v
+# --------------------------------------------------------------------------
+
+def attention_backward(q, k, v, do, *, causal: bool, scale: float):
+    """Gradients of the exact attention above, contracted with dO, in fp64.
+
+    The plain chain rule through O = P V, P = softmax(S), S = scale * Q K^T
+    (masked entries have P = 0), as restated in [LESSON] section "Обратный
+    проход: пересчитать дешевле, чем хранить":
+
+        dV = P^T dO          dP = dO V^T
+        dS = P * (dP - rowsum(P * dP))
+        dQ = scale * dS K    dK = scale * dS^T Q
+
+    with the row term taken from its definition, rowsum(P * dP), not from
+    the identity dO . O that a fast kernel uses.  Under GQA the gradients of
+    a kv head add up over its g query heads.  Returns (dq, dk, dv) shaped
+    like q, k, v.
+    """
+    q = as_f64(q)
+    k = as_f64(k)
+    v = as_f64(v)
+    do = as_f64(do)
+    B, Hq, Tq, d = q.shape
+    _, Hkv, Tk, _ = k.shape
+    g = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(Tq)[:, None]
+    cols = np.arange(Tk)[None, :]
+    vis = (cols <= rows) if causal else np.ones((Tq, Tk), bool)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            S = scale * (q[b, h] @ k[b, kh].T)
+            S = np.where(vis, S, _NEG_INF)
+            m = S.max(axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            E = np.where(vis, np.exp(S - m), 0.0)
+            l = E.sum(axis=1, keepdims=True)
+            P = np.divide(E, l, out=np.zeros_like(E), where=l > 0)
+            dP = do[b, h] @ v[b, kh].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dv[b, kh] += P.T @ do[b, h]
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
+# --------------------------------------------------------------------------
 # The online (tiled) fold -- a second, independent route to the same result
 # --------------------------------------------------------------------------
 

@@ -418,3 +418,107 @@ def test_decode_seqlens_seed0():
     assert sl.tolist() == [28027, 21244, 17250, 9588, 10796, 2324, 3412, 1548, 6587, 26841,
                            21639, 29999, 17011, 20281, 31840, 24181]
     assert int(sl.sum()) == 272568
+
+
+# ---------------------------------------------------------------------------
+# Backward pass ([LESSON] "Обратный проход: пересчитать дешевле, чем хранить")
+# ---------------------------------------------------------------------------
+
+BWD_SHAPES = [
+    # B, Hq, Hkv, Tq, Tk, d, causal
+    (1, 2, 2, 13, 13, 16, True),
+    (2, 4, 2, 20, 17, 8, False),
+    (1, 6, 2, 9, 30, 8, True),     # Tq < Tk, causal top-left
+    (1, 2, 1, 30, 9, 8, True),     # Tq > Tk
+    (1, 4, 1, 11, 11, 4, False),   # g = 4
+]
+
+
+@pytest.mark.parametrize("shape", BWD_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_matches_torch_autograd_fp64(shape):
+    """Library routine: torch autograd in fp64 through the naive masked
+    attention (the same check the lesson page runs)."""
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    rng = np.random.default_rng(11)
+    q, k, v, do = (_rand(rng, B, Hq, Tq, d), _rand(rng, B, Hkv, Tk, d),
+                   _rand(rng, B, Hkv, Tk, d), _rand(rng, B, Hq, Tq, d))
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    g = Hq // Hkv
+    kk = tk.repeat_interleave(g, dim=1)
+    vv = tv.repeat_interleave(g, dim=1)
+    S = scale * (tq @ kk.transpose(-1, -2))
+    if causal:
+        mask = torch.ones(Tq, Tk, dtype=torch.bool).tril()
+        S = S.masked_fill(~mask, float("-inf"))
+    O = torch.softmax(S, dim=-1) @ vv
+    O.backward(torch.tensor(do))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=causal, scale=scale)
+    assert np.max(np.abs(dq - tq.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dk - tk.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dv - tv.grad.numpy())) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(causal):
+    """Brute force: central differences of f(x) = <dO, O(x)> through the
+    forward oracle along random directions equal <grad, direction>."""
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, T, d = 1, 2, 1, 6, 4
+    q, k, v, do = (_rand(rng, B, Hq, T, d), _rand(rng, B, Hkv, T, d),
+                   _rand(rng, B, Hkv, T, d), _rand(rng, B, Hq, T, d))
+    scale = 0.7
+    grads = oracle.attention_backward(q, k, v, do, causal=causal, scale=scale)
+
+    def f(qq, kk, vv):
+        O, _ = oracle.softmax_attention(qq, kk, vv, causal=causal, scale=scale)
+        return float(np.sum(do * O))
+
+    eps = 1e-6
+    for which in range(3):
+        for _ in range(3):
+            args = [q.copy(), k.copy(), v.copy()]
+            direction = _rand(rng, *args[which].shape)
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which] += eps * direction
+            minus[which] -= eps * direction
+            fd = (f(*plus) - f(*minus)) / (2 * eps)
+            assert abs(fd - float(np.sum(grads[which] * direction))) < 1e-7
+
+
+def test_backward_invariants():
+    """Shifting every key by one vector leaves O unchanged, so the key
+    gradients of a head sum to zero; the row term rowsum(P * dP) equals
+    dO . O (the identity the lesson uses); dO = 0 gives zero gradients."""
+    rng = np.random.default_rng(13)
+    B, Hq, Hkv, T, d = 2, 4, 2, 24, 8
+    q, k, v, do = (_rand(rng, B, Hq, T, d), _rand(rng, B, Hkv, T, d),
+                   _rand(rng, B, Hkv, T, d), _rand(rng, B, Hq, T, d))
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=causal, scale=0.35)
+        assert np.max(np.abs(dk.sum(axis=2))) < 1e-12
+        z = oracle.attention_backward(q, k, v, np.zeros_like(do), causal=causal, scale=0.35)
+        assert all(np.all(x == 0) for x in z)
+    # D identity on one head, P recovered by using V = identity.
+    Tk = T
+    eye = np.eye(Tk).reshape(1, 1, Tk, Tk)
+    qq, kk = q[:1, :1], k[:1, :1]
+    P, _ = oracle.softmax_attention(qq, kk, eye, causal=True, scale=0.35)
+    O, _ = oracle.softmax_attention(qq, kk, v[:1, :1], causal=True, scale=0.35)
+    dP = do[0, 0] @ v[0, 0].T
+    assert np.max(np.abs((P[0, 0] * dP).sum(axis=1) - (do[0, 0] * O[0, 0]).sum(axis=1))) < 1e-12
+
+
+def test_backward_dv_closed_form():
+    """dO = all ones: dV_j = (sum_i P_ij) * ones -- the column sums of the
+    probabilities, obtained independently through the forward oracle with
+    V = identity."""
+    rng = np.random.default_rng(14)
+    T, d = 16, 8
+    q, k, v = _rand(rng, 1, 1, T, d), _rand(rng, 1, 1, T, d), _rand(rng, 1, 1, T, d)
+    P, _ = oracle.softmax_attention(q, k, np.eye(T).reshape(1, 1, T, T), causal=True, scale=0.4)
+    _, _, dv = oracle.attention_backward(q, k, v, np.ones((1, 1, T, d)), causal=True, scale=0.4)
+    colsum = P[0, 0].sum(axis=0)
+    assert np.max(np.abs(dv[0, 0] - colsum[:, None])) < 1e-12
