@@ -129,6 +129,28 @@ def prefill_case(torch, fa, w, steps, warmup, seed=0):
     return wall, ev_ms
 
 
+def backward_case(torch, fa, w, steps, warmup, seed=0):
+    """fa_bwd on the workload's shapes: q, k, v and dout N(0,1) (q times the
+    workload's multiplier), o and lse from one fa_fwd call.  Times the whole
+    call (row-term, dQ and dK/dV kernels)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    q = dev_normal(torch, (w.B, w.Hq, w.Tq, w.d), gen, w.q_mult)
+    k = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
+    v = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
+    do = dev_normal(torch, (w.B, w.Hq, w.Tq, w.d), gen)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.causal, w.scale, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    launch = fa.prepared("fa_bwd", q, k, v, o, lse, do, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Tq,
+                         w.Tk, w.d, int(w.causal), w.scale, stream=stream)
+    wall, ev_ms = time_calls(torch, launch, steps, warmup)
+    del q, k, v, do, o, lse, dq, dk, dv
+    return wall, ev_ms
+
+
 def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
     """Decode timed over `copies` independent caches used in rotation, so the
     last-level cache cannot serve one call's reads from the previous call."""
@@ -220,7 +242,9 @@ def cpu_baseline(w, budget_s=12.0, max_s=30.0):
 
 def inputs_names():
     from exact_tiled_attention_02_amd import inputs
-    return inputs.WORKLOADS.keys()
+    names = list(inputs.WORKLOADS.keys())
+    return names + ["bwd_" + n for n, w in inputs.WORKLOADS.items()
+                    if isinstance(w, inputs.Prefill) and w.dtype == "bf16"]
 
 
 def run_only(torch, fa, inputs, args):
@@ -233,6 +257,14 @@ def run_only(torch, fa, inputs, args):
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+    if args.only.startswith("bwd_"):
+        w = inputs.WORKLOADS[args.only[4:]]
+        wall, ev = backward_case(torch, fa, w, args.steps, args.warmup)
+        out = {"workload": "backward, " + w.name, "TFLOP/s": round(w.bwd_flops / wall / 1e12, 2),
+               "call_ms": round(ev, 4),
+               "frac_of_mfma_peak": round(w.bwd_flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        print(json.dumps(out), flush=True)
+        return
     w = inputs.WORKLOADS[args.only]
     if isinstance(w, inputs.Prefill):
         wall, ev = prefill_case(torch, fa, w, args.steps, args.warmup)
@@ -316,6 +348,16 @@ def main():
                           "frac_of_mfma_peak": round(ach / PEAK_BF16_TFLOPS, 4),
                           "traffic": measured_traffic(name)}
             log(f"[bench]   {also[name]}")
+        for name, steps in (("gpt2_small_mha", 20), ("qwen3_0p6b_gqa", 20), ("llama3_8b_long", 3)):
+            wk = inputs.WORKLOADS[name]
+            log(f"[bench] backward, {wk.name}")
+            wl, ev = backward_case(torch, fa, wk, steps, 2)
+            ach = wk.bwd_flops / (ev * 1e-3) / 1e12
+            also["bwd_" + name] = {"value": round(wk.bwd_flops / wl / 1e12, 2), "unit": "TFLOP/s",
+                                   "flops": "10*B*Hq*Tq*Tk*d/2 (five products, causal)",
+                                   "ms_per_call": round(wl * 1e3, 4), "call_ms_events": round(ev, 4),
+                                   "frac_of_mfma_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+            log(f"[bench]   {also['bwd_' + name]}")
         wd = inputs.FLASH_DECODE
         S = fa.fa_decode_workgroups(wd.B, wd.Hq, wd.Hkv, wd.Tk_max, wd.d, args.decode_splits)
         log(f"[bench] {wd.name}, {S} key ranges")

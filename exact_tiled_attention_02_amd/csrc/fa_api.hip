@@ -24,6 +24,31 @@ std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
 int map_err(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
+// A library-owned device buffer of at least `need` bytes for calls on
+// `stream` of the current device: grown (by a quarter more than asked) with
+// stream-ordered allocation, kept for the next call.
+int workspace(hipStream_t stream, size_t need, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
+  if (w.bytes < need) {
+    if (w.ptr != nullptr) {
+      if (hipFreeAsync(w.ptr, stream) != hipSuccess) return FA_ERR_ALLOC;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    const size_t grow = need + need / 4;
+    if (hipMallocAsync(&w.ptr, grow, stream) != hipSuccess) {
+      w.ptr = nullptr;
+      return FA_ERR_ALLOC;
+    }
+    w.bytes = grow;
+  }
+  *out = (char*)w.ptr;
+  return FA_OK;
+}
+
 int check_fwd(const void* q, const void* k, const void* v, const void* o, int B, int Hq, int Hkv,
               int Tq, int Tk, int d, float scale, bool* empty) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_SHAPE;
@@ -115,6 +140,56 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return map_err(fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
 }
 
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk,
+           int d, int causal, float scale, void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Hq == 0 || (Tq == 0 && Tk == 0)) return FA_OK;
+  if (Tq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
+    return FA_ERR_NULL;
+  if (Tk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return FA_ERR_NULL;
+  // Byte ranges of one (batch, head) plane are 32-bit; workgroup counts
+  // (tiles x heads) must fit the grid.
+  if ((int64_t)Tq * d * 4 > INT32_MAX || (int64_t)Tk * d * 4 > INT32_MAX) return FA_ERR_SHAPE;
+  const int64_t Tqp = ((int64_t)Tq + fa::kBwdRowPad - 1) / fa::kBwdRowPad * fa::kBwdRowPad;
+  if ((int64_t)B * Hq * ((Tq + 127) / 128) > INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * ((Tk + 127) / 128) > INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq * Tqp / 16 > INT32_MAX) return FA_ERR_SHAPE;
+
+  hipStream_t hs = (hipStream_t)stream;
+  const size_t rows = (size_t)B * Hq * (size_t)Tqp;
+  char* ws = nullptr;
+  if (rows > 0) {
+    const int wst = workspace(hs, 2 * rows * sizeof(float), &ws);
+    if (wst != FA_OK) return wst;
+  }
+  fa::BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.l2 = (float*)ws;
+  p.delta = ws != nullptr ? (float*)ws + rows : nullptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  p.Tqp = (int)Tqp;
+  p.g = Hq / Hkv;
+  p.c = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+  return map_err(fa::launch_bwd(p, d, causal != 0, hs));
+}
+
 int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0 || Hq % Hkv != 0)
     return -FA_ERR_SHAPE;
@@ -143,27 +218,9 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   const size_t need = cum_bytes + nparts * (size_t)(d + 2) * sizeof(float);
   hipStream_t hs = (hipStream_t)stream;
 
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
   char* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[std::make_pair(dev, hs)];
-    if (w.bytes < need) {
-      if (w.ptr != nullptr) {
-        if (hipFreeAsync(w.ptr, hs) != hipSuccess) return FA_ERR_ALLOC;
-        w.ptr = nullptr;
-        w.bytes = 0;
-      }
-      const size_t grow = need + need / 4;
-      if (hipMallocAsync(&w.ptr, grow, hs) != hipSuccess) {
-        w.ptr = nullptr;
-        return FA_ERR_ALLOC;
-      }
-      w.bytes = grow;
-    }
-    ws = (char*)w.ptr;
-  }
+  const int wst = workspace(hs, need, &ws);
+  if (wst != FA_OK) return wst;
 
   fa::DecodeParams p{};
   p.q = q;
@@ -199,7 +256,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape or size argument";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (64 or 128)";
-    case FA_ERR_ALLOC: return "decode workspace allocation failed";
+    case FA_ERR_ALLOC: return "workspace allocation failed";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_DEVICE: return "no usable HIP device";
     default: return "unknown status";

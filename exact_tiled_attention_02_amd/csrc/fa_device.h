@@ -69,9 +69,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_char_t*)p;
 }
 
-// Copy 16 bytes per lane from a buffer resource (byte offset voff + soff;
-// past the resource's size the data read is zero) straight into LDS at
-// lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
+// Copy 16 bytes per lane from a buffer resource (byte offset voff + soff)
+// straight into LDS at lds_base + 16 * lane (lds_base must be the same for
+// the whole wavefront).  A lane whose voff is at or past the resource's size
+// reads zeros; the scalar soff is not part of that range check, so callers
+// that rely on it keep soff = 0 and put every offset into voff.
 __device__ __forceinline__ void copy16_buf_to_lds(__amdgpu_buffer_rsrc_t rsrc, void* lds_base,
                                                   uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voff, soff, 0, 0);

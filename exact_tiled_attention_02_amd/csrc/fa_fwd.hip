@@ -48,6 +48,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_lds.h"
 
 namespace fa {
 namespace {
@@ -79,56 +80,6 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-
-template <int V>
-using IC = std::integral_constant<int, V>;
-
-// Calls f(IC<I>{}) for I = B .. E-1 (compile-time unrolled).
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(IC<B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-
-
-// Copy 16 bytes per lane from global memory straight into LDS at
-// lds_base + 16 * lane (lds_base must be the same for the whole wavefront).
-__device__ __forceinline__ void copy16_to_lds(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16) at addr + OFF bytes:
-// within each group of 16 lanes, output lane 4*q + e receives element e of
-// the 8 bytes addressed by input lanes q, q + 4, q + 8, q + 12 (in that
-// order).  Issued as inline assembly: through the compiler builtin every such
-// read would first wait for all outstanding global->LDS copies (which target
-// the other LDS stage).  The result is not usable until lds_tr_wait() has
-// run on it.
-template <int OFF>
-__device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-
-// 16-byte LDS read at addr + OFF bytes, issued as inline assembly so that
-// its place in the instruction stream (how far ahead of its use) is fixed
-// here rather than by the scheduler; not usable before lds_wait_tie().
-template <int OFF>
-__device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
-  bf16x8 r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
-  return r;
-}
-// Wait until at most N LDS reads of this wavefront are outstanding, tied to
-// the operand that needed the wait.
-template <int N>
-__device__ __forceinline__ void lds_wait_tie(bf16x8& v) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
-}
 
 // Wait until at most N LDS reads of this wavefront are outstanding (they
 // complete in issue order); the operand group passed in is tied to the wait
@@ -248,7 +199,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   // Copy r of wavefront w fills LDS chunks [(r*NW + w)*64, +64) of a tile;
   // chunk L is row L / CPR, physical chunk L % CPR, which holds logical
   // chunk (L % CPR) ^ swizzle(row).  Lane byte offsets within a tile are
-  // constants; the tile start is a scalar offset.
+  // constants; the tile start is added to them (not passed as the scalar
+  // offset, which the buffer range check does not include).
   const int nbytes = p.Tk * D * 2;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, nbytes, 0x00020000);
@@ -268,8 +220,8 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     bf16* Vd = lds + (kStages + st) * TILE;
 #pragma unroll
     for (int r = 0; r < NCOPY; ++r) {
-      copy16_buf_to_lds(krsrc, Kd + (r * NW + wave) * 512, ksrc[r], soff);
-      copy16_buf_to_lds(vrsrc, Vd + (r * NW + wave) * 512, vsrc[r], soff);
+      copy16_buf_to_lds(krsrc, Kd + (r * NW + wave) * 512, ksrc[r] + soff, 0);
+      copy16_buf_to_lds(vrsrc, Vd + (r * NW + wave) * 512, vsrc[r] + soff, 0);
     }
   };
   // Wait until the copies of tile t (issued `later` tiles before the newest

@@ -43,7 +43,33 @@ struct DecodeParams {
   float c;         // log2(e) / sqrt(d)
 };
 
+// One backward call.  q, o, dout, dq: [B,Hq,Tq,d]; k, v, dk, dv: [B,Hkv,Tk,d];
+// all bf16.  l2 and delta are library workspace, [B*Hq, Tqp] fp32 each.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B,Hq,Tq] natural-log row log-sum-exp of the forward
+  void* dq;
+  void* dk;
+  void* dv;
+  float* l2;         // lse * log2(e) per query row; 0 on padding rows
+  float* delta;      // dO_i . O_i per query row; 0 on padding rows
+  int B, Hq, Hkv, Tq, Tk;
+  int Tqp;           // Tq rounded up to a multiple of kBwdRowPad
+  int g;             // Hq / Hkv
+  float c;           // scale * log2(e) (signed)
+  float scale;
+};
+
+// Rows of each (batch, head) plane of the backward workspace are padded to a
+// multiple of this, so that whole query tiles of it can be read unchecked.
+constexpr int kBwdRowPad = 256;
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
 // Workgroups that the decode kernel for (d, hpw) keeps resident on the

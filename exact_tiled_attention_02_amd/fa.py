@@ -1,6 +1,6 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_decode``, ``fa_decode_workgroups``,
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
 ``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
 with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd.restype = I
         lib.fa_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         lib.fa_fwd_f32.restype = I
+        lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        lib.fa_bwd.restype = I
         lib.fa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         lib.fa_decode.restype = I
         lib.fa_decode_workgroups.argtypes = [I, I, I, I, I, I]
@@ -103,6 +105,13 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
     _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk,
                              d, int(bool(causal)), float(scale), _stream(stream)), "fa_fwd_f32")
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale,
+           stream=None) -> None:
+    _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                         _ptr(dk), _ptr(dv), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
+                         float(scale), _stream(stream)), "fa_bwd")
 
 
 def fa_decode(q, kcache, vcache, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits, stream=None) -> None:
@@ -208,3 +217,29 @@ def decode(q, kcache, vcache, seqlens, *, num_splits: int = 0, out=None, stream=
         stream = torch.cuda.current_stream(q.device)
     fa_decode(q, kcache, vcache, seqlens, out, B, Hq, Hkv, Tmax, d, num_splits, stream)
     return out
+
+
+def attention_backward(q, k, v, o, lse, dout, *, causal: bool, scale: float | None = None,
+                       dq=None, dk=None, dv=None, stream=None):
+    """Gradients (dq, dk, dv) of ``attention`` for bf16 [B,H,T,d] cuda tensors,
+    from the forward's o and lse (``fa_bwd``)."""
+    import torch
+    _require(all(t.dim() == 4 and t.is_cuda and t.is_contiguous() and t.dtype == torch.bfloat16
+                 for t in (q, k, v, o, dout)),
+             "q, k, v, o, dout must be contiguous bf16 [B,H,T,d] cuda tensors")
+    _require(lse.dtype == torch.float32 and lse.is_cuda and lse.is_contiguous(),
+             "lse must be contiguous fp32 on the GPU")
+    B, Hq, Tq, d = q.shape
+    Bk, Hkv, Tk, dk_ = k.shape
+    _require(Bk == B and dk_ == d and tuple(v.shape) == tuple(k.shape), "shape mismatch")
+    _require(tuple(o.shape) == tuple(q.shape) == tuple(dout.shape), "o/dout shape mismatch")
+    _require(tuple(lse.shape) == (B, Hq, Tq), "lse must be [B,Hq,Tq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream)
+    return dq, dk, dv

@@ -8,7 +8,8 @@ Recipe (the same for every workload):
 
 * ``rng = numpy.random.default_rng(seed)``; every tensor is drawn with
   ``rng.standard_normal(shape, dtype=float32)`` in the order the workload
-  lists them (prefill: q, k, v; decode: seqlens first, then q, k-cache,
+  lists them (prefill: q, k, v, and for the backward pass the output
+  gradient dout after them; decode: seqlens first, then q, k-cache,
   v-cache).
 * An optional query multiplier (3.0 for the Qwen3-0.6B-shaped workload, 100
   for the stability case) is applied in fp32 *before* rounding.
@@ -78,6 +79,13 @@ class Prefill:
         """Attention FLOPs, 4*B*Hq*Tq*Tk*d, halved for causal."""
         f = 4.0 * self.B * self.Hq * self.Tq * self.Tk * self.d
         return f / 2 if self.causal else f
+
+    @property
+    def bwd_flops(self) -> float:
+        """Backward FLOPs: the five products S = QK^T (recomputed), dP = dO V^T,
+        dV = P^T dO, dQ = dS K, dK = dS^T Q, i.e. 10*B*Hq*Tq*Tk*d, halved
+        for causal (2.5 times the forward's)."""
+        return 2.5 * self.flops
 
     @property
     def min_bytes(self) -> int:
@@ -151,6 +159,17 @@ def prefill_inputs(w: Prefill, *, seed: Optional[int] = None):
     k = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
     v = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
     return q, k, v
+
+
+def prefill_inputs_with_grad(w: Prefill, *, seed: Optional[int] = None):
+    """(q, k, v, dout): q, k, v exactly as prefill_inputs draws them, then the
+    output gradient dout [B,Hq,Tq,d] drawn next from the same generator."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = _draw(rng, (w.B, w.Hq, w.Tq, w.d), w.dtype, w.q_mult)
+    k = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
+    v = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), w.dtype)
+    do = _draw(rng, (w.B, w.Hq, w.Tq, w.d), w.dtype)
+    return q, k, v, do
 
 
 def decode_seqlens(w: Decode, *, seed: Optional[int] = None) -> np.ndarray:

@@ -44,7 +44,7 @@ typedef enum {
   FA_ERR_NULL = 1,         /* a required pointer is NULL                      */
   FA_ERR_SHAPE = 2,        /* negative size, Hq not a multiple of Hkv, ...    */
   FA_ERR_UNSUPPORTED = 3,  /* head dimension other than 64 or 128             */
-  FA_ERR_ALLOC = 4,        /* the decode workspace could not be allocated     */
+  FA_ERR_ALLOC = 4,        /* a library workspace could not be allocated     */
   FA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch        */
   FA_ERR_DEVICE = 6        /* no usable HIP device / runtime error            */
 } fa_status;
@@ -91,6 +91,49 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
                void* stream);
+
+/*
+ * fa_bwd -- gradients of fa_fwd (training backward pass), bf16 in/out.
+ *
+ * Given the forward's inputs q, k, v, its output o and row log-sum-exp lse
+ * (as fa_fwd wrote them, same causal flag and scale) and the gradient dout
+ * of a loss with respect to o, computes the gradients with respect to q, k
+ * and v by the recomputation of [LESSON] section "Обратный проход:
+ * пересчитать дешевле, чем хранить": score tiles are computed again,
+ * P_ij = exp(scale * q_i.k_j - lse_i) restores the probabilities without
+ * normalising, and with D_i = dout_i . o_i
+ *     dv_j = sum_i P_ij dout_i,          dP_ij = dout_i . v_j,
+ *     dS_ij = P_ij (dP_ij - D_i),
+ *     dq_i = scale * sum_j dS_ij k_j,    dk_j = scale * sum_i dS_ij q_i,
+ * over the (i, j) pairs visible under the same mask as fa_fwd.  With
+ * grouped-query attention ([NOTE] section "Prefill i dekodowanie to różne
+ * problemy") dk and dv of kv head kh sum the contributions of its g = Hq/Hkv
+ * query heads.  Nothing of size Tq x Tk is stored.
+ *
+ *   q, o, dout, dq : [B, Hq,  Tq, d] bf16     lse : [B, Hq, Tq] fp32
+ *   k, v, dk, dv   : [B, Hkv, Tk, d] bf16     d   : 64 or 128
+ *
+ * dq, dk and dv are fully overwritten (rounded to nearest even); keys that
+ * no query sees get dk = dv = 0.  Arithmetic: bf16 matrix products with fp32
+ * accumulation; P and dS are rounded to bf16 before the products that
+ * consume them; D_i, the exponentials and the masking in fp32.  The result
+ * is deterministic (no atomics; every output element is summed in a fixed
+ * order).
+ *
+ * Workspace: D_i and lse_i * log2(e) per query row (2 * B * Hq * Tqp fp32,
+ * Tqp = Tq rounded up to a multiple of 256) in the library-owned buffer of
+ * (device, stream) that fa_decode also uses, grown on demand with
+ * stream-ordered allocation; fa_release_workspace() frees it.
+ * B == 0, Hq == 0 or Tq == Tk == 0 is a valid empty call.  Tq == 0 gives
+ * dk = dv = 0 (q, o, lse, dout and dq may then be NULL); Tk == 0 gives
+ * dq = 0 (k, v, dk and dv may then be NULL).  Errors: FA_ERR_NULL,
+ * FA_ERR_SHAPE (negative sizes, Hkv < 1, Hq % Hkv != 0, non-finite scale,
+ * sizes whose workgroup counts overflow), FA_ERR_UNSUPPORTED (d not 64/128),
+ * FA_ERR_ALLOC, FA_ERR_DEVICE, FA_ERR_LAUNCH.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq,
+           int Tk, int d, int causal, float scale, void* stream);
 
 /*
  * fa_decode -- single-query attention over a KV cache with split-KV

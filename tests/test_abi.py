@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_strerror", "fa_release_workspace",
-              "fa_decode_workgroups", "fa_read_probe"):
+    for n in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_decode", "fa_strerror",
+              "fa_release_workspace", "fa_decode_workgroups", "fa_read_probe"):
         assert n in names
 
 
@@ -64,6 +64,30 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 def test_fwd_validation(lib, entry, args, status):
     fn = getattr(lib, entry)
     assert fn(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale)
+    ((FAKE,) * 9 + (1, 4, 2, 8, 8, 96, 1, 0.1), 3),                 # d unsupported
+    ((FAKE,) * 9 + (1, 4, 3, 8, 8, 64, 1, 0.1), 2),                 # Hq % Hkv
+    ((FAKE,) * 9 + (1, 4, 0, 8, 8, 64, 1, 0.1), 2),                 # Hkv = 0
+    ((FAKE,) * 9 + (-1, 4, 2, 8, 8, 64, 1, 0.1), 2),                # negative B
+    ((FAKE,) * 9 + (1, 4, 2, -1, 8, 64, 1, 0.1), 2),                # negative Tq
+    ((FAKE,) * 9 + (1, 4, 2, 8, -1, 64, 1, 0.1), 2),                # negative Tk
+    ((FAKE,) * 9 + (1, 4, 2, 8, 8, 64, 1, float("nan")), 2),
+    ((FAKE,) * 4 + (P,) + (FAKE,) * 4 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # lse NULL
+    ((FAKE,) * 5 + (P,) + (FAKE,) * 3 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # dout NULL
+    ((FAKE,) * 6 + (P,) + (FAKE,) * 2 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # dq NULL
+    ((FAKE,) * 7 + (P, FAKE) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),            # dk NULL
+    ((FAKE,) * 8 + (P,) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),                 # dv NULL
+    ((P, FAKE, FAKE, P, P, P, P, P, FAKE) + (1, 4, 2, 0, 8, 64, 1, 0.1), 1),     # Tq = 0: dk still needed
+    ((P,) * 9 + (0, 4, 2, 8, 8, 64, 1, 0.1), 0),                    # empty batch
+    ((P,) * 9 + (2, 4, 2, 0, 0, 64, 0, 0.1), 0),                    # no rows, no keys
+    ((FAKE,) * 9 + (1, 1, 1, (1 << 31) // 512 + 1, 8, 128, 1, 0.1), 2),   # plane over 2^31 bytes
+    ((FAKE,) * 9 + (1 << 20, 1 << 10, 1, 256, 8, 64, 0, 0.1), 2),  # grid overflow
+], ids=lambda a: "case" if isinstance(a, tuple) else str(a))
+def test_bwd_validation(lib, args, status):
+    assert lib.fa_bwd(*args, None) == status
 
 
 @pytest.mark.parametrize("args,status", [
