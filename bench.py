@@ -41,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["exact_tiled_attention_02_amd/csrc/fa_fwd.hip",
                 "exact_tiled_attention_02_amd/csrc/fa_device.h",
+                "exact_tiled_attention_02_amd/csrc/fa_lds.h",
                 "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
     "decode": ["exact_tiled_attention_02_amd/csrc/fa_decode.hip",
                "exact_tiled_attention_02_amd/csrc/fa_device.h",

@@ -46,6 +46,8 @@
 #include "fa_launch.h"
 #include "fa_lds.h"
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -53,7 +55,6 @@ constexpr int kDkdvThreads = 256;  // 4 wavefronts, 32 keys each
 constexpr int kKeysPerWg = 128;    // keys per dK/dV workgroup
 constexpr int kQTile = 64;         // query rows per LDS stage (dK/dV kernel)
 constexpr int kKTile = 64;         // keys per LDS stage (dQ kernel)
-constexpr int kDqWaves = 4;        // wavefronts per dQ workgroup
 constexpr int kPrepThreads = 256;
 
 // ---------------------------------------------------------------------------
@@ -291,14 +292,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   const float c = p.c;
 
   // 32 query rows (half HF of the stage-ST tile whose first row is q0).
-  auto rows32 = [&](int q0, auto st_c, auto hf_c) __attribute__((always_inline)) {
+  // MK: 0 no mask, 1 mask, 2 decided at run time by mask_rt (one code path;
+  // at d = 128 separate paths cost registers and were slower).
+  auto rows32 = [&](int q0h, auto st_c, auto hf_c, auto mk_c, bool mask_rt) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int HF = decltype(hf_c)::value;
-    const int q0h = q0 + 32 * HF;
-    // Under the causal mask query i sees key j iff j <= i; kw and q0h are
-    // multiples of 32.
-    if (CAUSAL && q0h < kw) return;   // every key of this wavefront is after every row
-    const bool mask = (CAUSAL && q0h == kw) || q0h + 32 > p.Tq;
+    constexpr int MK = decltype(mk_c)::value;
     constexpr int QT = QOFF + ST * SB + HF * 32 * D * 2;   // Q rows of this half
     constexpr int GT = QT + TB;                            // dO rows
     constexpr int LT = ST * LDB + HF * 32 * 4;             // L rows; D at +256
@@ -333,16 +332,21 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     // P = exp(S*scale - L) (base 2), dS = P (dP - D).
     float pv[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = exp2_fast(fmaf(sc[r], c, -lv[r >> 2][r & 3]));
-      if (mask) {
-        const int qi = q0h + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = qi < p.Tq && (!CAUSAL || my_k <= qi);
-        x = vis ? x : 0.f;
+    for (int r = 0; r < 16; ++r) pv[r] = exp2_fast(fmaf(sc[r], c, -lv[r >> 2][r & 3]));
+    if (MK == 1 || (MK == 2 && mask_rt)) {
+      // Row offsets 8*(r/4) + r%4 outside [lo, hi) are masked: rows past
+      // Tq, and under the causal mask rows before this lane's key.
+      const int base = q0h + 4 * half;
+      const int lo = CAUSAL ? my_k - base : -64;
+      const int hi = p.Tq - base;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        pv[r] = (off >= lo && off < hi) ? pv[r] : 0.f;
       }
-      pv[r] = x;
-      ds[r] = x * (dp[r] - dl[r >> 2][r & 3]);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = pv[r] * (dp[r] - dl[r >> 2][r & 3]);
     const bf16x8 pb[2] = {pack8(pv), pack8(pv + 8)};
     const bf16x8 sb[2] = {pack8(ds), pack8(ds + 8)};
 
@@ -400,8 +404,20 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     tile_barrier();
     if (it + 1 < nit) issue(it + 1, IC<ST ^ 1>{});
     const int q0 = qs + (it % ntq) * kQTile;
-    rows32(q0, st_c, IC<0>{});
-    rows32(q0, st_c, IC<1>{});
+    static_for<0, 2>([&](auto hf_c) {
+      const int q0h = q0 + 32 * hf_c;
+      // Under the causal mask query i sees key j iff j <= i; kw and q0h are
+      // multiples of 32.  Blocks with every key after every row are skipped;
+      // only the diagonal block and the last rows need the mask.
+      if (CAUSAL && q0h < kw) return;
+      const bool mask = (CAUSAL && q0h == kw) || q0h + 32 > p.Tq;
+      if constexpr (D == 128)
+        rows32(q0h, st_c, hf_c, IC<2>{}, mask);
+      else if (mask)
+        rows32(q0h, st_c, hf_c, IC<1>{}, true);
+      else
+        rows32(q0h, st_c, hf_c, IC<0>{}, false);
+    });
   };
   if (nit > 0) issue(0, IC<0>{});
   for (int it = 0; it < nit; it += 2) {
@@ -423,9 +439,8 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
 // ---------------------------------------------------------------------------
 // 3. dQ
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64 * kDqWaves, 1) bwd_dq_kernel(const BwdParams p) {
-  constexpr int NW = kDqWaves;
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) bwd_dq_kernel(const BwdParams p) {
   constexpr int NT = 64 * NW;
   constexpr int BM = 32 * NW;                  // query rows per workgroup
   constexpr int NC = D / 16;
@@ -502,12 +517,11 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) bwd_dq_kernel(const BwdParam
   const float c = p.c;
 
   // 32 keys (block KB of the stage-ST tile whose first key is t*kKTile).
-  auto keys32 = [&](int t, auto st_c, auto kb_c) __attribute__((always_inline)) {
+  // MK as in the dK/dV kernel.
+  auto keys32 = [&](int kb0, auto st_c, auto kb_c, auto mk_c, bool mask_rt) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value;
     constexpr int KB = decltype(kb_c)::value;
-    const int kb0 = t * kKTile + 32 * KB;
-    if (CAUSAL && kb0 > q0w + 31) return;   // every key after every row
-    const bool mask = kb0 + 32 > p.Tk || (CAUSAL && kb0 + 31 > q0w);
+    constexpr int MK = decltype(mk_c)::value;
     constexpr int KT = ST * SB + KB * 32 * D * 2;
     constexpr int VT = KT + TB;
 
@@ -536,17 +550,22 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) bwd_dq_kernel(const BwdParam
       va[db_c][1] = lds_read_tr<KT>(rd.tr[1][db_c]);
     });
 
-    float ds[16];
+    float pv[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = exp2_fast(fmaf(sc[r], c, -l2));
-      if (mask) {
-        const int kj = kb0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = kj < p.Tk && (!CAUSAL || kj <= my_q);
-        x = vis ? x : 0.f;
+    for (int r = 0; r < 16; ++r) pv[r] = exp2_fast(fmaf(sc[r], c, -l2));
+    if (MK == 1 || (MK == 2 && mask_rt)) {
+      // Key offsets 8*(r/4) + r%4 at or past hi are masked: keys past Tk,
+      // and under the causal mask keys after this lane's row.
+      const int base = kb0 + 4 * half;
+      const int hi = CAUSAL ? min(p.Tk, my_q + 1) - base : p.Tk - base;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        pv[r] = off < hi ? pv[r] : 0.f;
       }
-      ds[r] = x * (dp[r] - dl);
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ds[r] = pv[r] * (dp[r] - dl);
     const bf16x8 sb[2] = {pack8(ds), pack8(ds + 8)};
 
     // dQ^T += K^T dS^T over the 32 keys in two 16-key steps.
@@ -578,8 +597,17 @@ __global__ void __launch_bounds__(64 * kDqWaves, 1) bwd_dq_kernel(const BwdParam
     tile_barrier();
     if (t + 1 < ntiles) issue(t + 1, IC<ST ^ 1>{});
     if (t < my_tiles) {
-      keys32(t, st_c, IC<0>{});
-      keys32(t, st_c, IC<1>{});
+      static_for<0, 2>([&](auto kb_c) {
+        const int kb0 = t * kKTile + 32 * kb_c;
+        if (CAUSAL && kb0 > q0w + 31) return;   // every key after every row
+        const bool mask = kb0 + 32 > p.Tk || (CAUSAL && kb0 + 31 > q0w);
+        if constexpr (D == 128)
+          keys32(kb0, st_c, kb_c, IC<2>{}, mask);
+        else if (mask)
+          keys32(kb0, st_c, kb_c, IC<1>{}, true);
+        else
+          keys32(kb0, st_c, kb_c, IC<0>{}, false);
+      });
     }
   };
   if (ntiles > 0) issue(0, IC<0>{});
@@ -602,9 +630,16 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
     const long long rows = (long long)p.B * p.Hq * p.Tqp;
     hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
                        dim3(kPrepThreads), 0, stream, p);
-    const int nqt = (p.Tq + 32 * kDqWaves - 1) / (32 * kDqWaves);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)nqt * p.B * p.Hq),
-                       dim3(64 * kDqWaves), 0, stream, p);
+    // 8 wavefronts (256 rows) per workgroup share each K/V tile; on grids
+    // too small to fill the device twice over, 4 (128 rows) balance better.
+    const long long heads = (long long)p.B * p.Hq;
+    const long long n8 = (p.Tq + 255) / 256 * heads;
+    if (n8 >= 2 * compute_units()) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 8>), dim3((unsigned)n8), dim3(512), 0, stream, p);
+    } else {
+      const long long n4 = (p.Tq + 127) / 128 * heads;
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, 4>), dim3((unsigned)n4), dim3(256), 0, stream, p);
+    }
   }
   if (p.Tk > 0) {
     const int nkb = (p.Tk + kKeysPerWg - 1) / kKeysPerWg;

@@ -552,21 +552,6 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
   }
 }
 
-// Compute units of the current device (cached per device; 256 if the query
-// fails).
-int compute_units() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_hg(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;

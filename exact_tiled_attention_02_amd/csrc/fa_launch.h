@@ -68,6 +68,10 @@ struct BwdParams {
 // multiple of this, so that whole query tiles of it can be read unchecked.
 constexpr int kBwdRowPad = 256;
 
+// Compute units of the current device (cached per device; 256 if the query
+// fails).
+int compute_units();
+
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);

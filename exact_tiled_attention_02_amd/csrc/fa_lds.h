@@ -62,6 +62,14 @@ __device__ __forceinline__ f32x4 lds_read_f32x4(uint32_t addr) {
   return r;
 }
 
+// 16-byte LDS write of four fp32 values at addr + OFF bytes (inline assembly,
+// so that the compiler does not first wait for the global->LDS copies in
+// flight).  Complete once an lgkmcnt wait has covered it.
+template <int OFF>
+__device__ __forceinline__ void lds_write_f32x4(uint32_t addr, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(addr), "v"(v), "n"(OFF) : "memory");
+}
+
 // Wait until at most N LDS reads of this wavefront are outstanding, tied to
 // the operand that needed the wait.
 template <int N>

@@ -310,3 +310,38 @@ def test_bwd_llama3_long_workload_sampled():
         bound = 2.0 ** -8 * (np.abs(full[0, kh, lo:]) + np.abs(share).sum(axis=0)) * 1.25 + 1e-6
         print(f"  {name} group sum: max err/bound = {np.max(err / bound):.3f}", flush=True)
         assert np.all(err <= bound)
+
+
+def test_bwd_large_grid_sampled_group():
+    """A grid large enough for the 8-wavefront dQ workgroups (B=2, Hq=32,
+    Hkv=8, T=2048, d=64, causal); the oracle checks every element of the
+    kv-head group 1 of sequence 1 (query heads 4..7)."""
+    from exact_tiled_attention_02_amd import fa
+    w = inputs.Prefill("t", B=2, Hq=32, Hkv=8, Tq=2048, Tk=2048, d=64, causal=True, seed=17)
+    q, k, v, do = inputs.prefill_inputs_with_grad(w)
+    b, kh, heads = 1, 1, [4, 5, 6, 7]
+    qs, ks, vs, dos = (q[b:b + 1, heads], k[b:b + 1, kh:kh + 1], v[b:b + 1, kh:kh + 1],
+                       do[b:b + 1, heads])
+    O, L = oracle.softmax_attention(qs, ks, vs, causal=True, scale=w.scale)
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o = torch.empty(tq.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(tq.shape[:3], dtype=torch.float32, device="cuda")
+    say("fa_fwd large grid")
+    fa.fa_fwd(tq, tk, tv, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, True, w.scale,
+              torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    lse32 = lse.cpu().numpy().copy()
+    o_bits[b:b + 1, heads] = to_bf16_bits(O)
+    lse32[b:b + 1, heads] = L.astype(np.float32)
+    say("fa_bwd large grid")
+    dq, dk, dv = run_bwd(q, k, v, o_bits, lse32, do, True, w.scale)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    rq, rk, rv = oracle.attention_backward(qs, ks, vs, dos, causal=True, scale=w.scale)
+    bq, bk, bv = bwd_error_bounds(oracle.as_f64(qs), oracle.as_f64(ks), oracle.as_f64(vs),
+                                  oracle.as_f64(dos), O, L, oracle.as_f64(o_bits[b:b + 1, heads]),
+                                  lse32[b:b + 1, heads].astype(np.float64), causal=True,
+                                  scale=w.scale)
+    check_bounded("dq", dq[b:b + 1, heads], rq, bq)
+    check_bounded("dk", dk[b:b + 1, kh:kh + 1], rk, bk)
+    check_bounded("dv", dv[b:b + 1, kh:kh + 1], rv, bv)
