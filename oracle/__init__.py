@@ -27,4 +27,5 @@ from .attention import (  # noqa: F401
     online_normalizer,
     online_weighted_sum,
     causal_block_pairs,
+    causal_offset,
 )

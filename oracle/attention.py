@@ -20,14 +20,22 @@ Visibility of key j to query row i:
     causal       j <= i -- top-left alignment, i.e. the strict upper triangle
                  of the n x m score matrix is masked ([FUSED07],
                  "FlashAttention-наив на numpy", reference attention)
+    causal, bottom-right alignment
+                 j <= i + (Tk - Tq): query row i sits at absolute position
+                 Tk - Tq + i of a sequence whose first Tk - Tq positions
+                 are already in the key/value cache (chunked prefill; with
+                 Tq = 1 this is the decode rule, where the new token sees
+                 every cached key -- [NOTE] section "Prefill i dekodowanie
+                 to różne problemy").  With Tq > Tk the first Tq - Tk rows
+                 see no key.
     decode       j < seqlens[b]; one query row; scale = 1/sqrt(d)
 
 Grouped-query attention: query head hq reads kv head hq // g, g = Hq / Hkv
 ([NOTE] section "Prefill i dekodowanie to różne problemy": g query heads share
 one KV head).  This is the same as repeating every kv head g times.
 
-A row with no visible key (only possible for Tk == 0 or seqlen == 0) is
-defined as O = 0, lse = -inf.
+A row with no visible key (Tk == 0, seqlen == 0, or the first Tq - Tk rows
+under bottom-right alignment) is defined as O = 0, lse = -inf.
 
 Arithmetic is IEEE fp64 throughout; inputs arrive as the exact bf16 bit
 patterns (uint16) or fp32 values that the GPU receives and are widened
@@ -59,6 +67,17 @@ def as_f64(x: np.ndarray) -> np.ndarray:
     if x.dtype in (np.float32, np.float64):
         return x.astype(np.float64)
     raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+_ALIGNS = ("top_left", "bottom_right")
+
+
+def causal_offset(Tq: int, Tk: int, align: str) -> int:
+    """Key j is visible to query row i under the causal mask iff
+    j <= i + causal_offset(Tq, Tk, align)."""
+    if align not in _ALIGNS:
+        raise ValueError(f"unknown causal alignment {align!r}")
+    return Tk - Tq if align == "bottom_right" else 0
 
 
 # --------------------------------------------------------------------------
@@ -95,14 +114,15 @@ def _rows_three_pass(Qr: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,
     return O, lse
 
 
-def softmax_attention(q, k, v, *, causal: bool, scale: float,
-                      row_chunk: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+def softmax_attention(q, k, v, *, causal: bool, scale: float, row_chunk: int = 256,
+                      align: str = "top_left") -> Tuple[np.ndarray, np.ndarray]:
     """Exact attention for q:[B,Hq,Tq,d], k,v:[B,Hkv,Tk,d] -> (O, lse) in fp64.
 
     Rows are independent, so they are evaluated in chunks of ``row_chunk`` to
     bound memory; under the causal mask a chunk ending at row r only needs
-    keys j <= r, so the keys beyond are left out (every one of them would be
-    masked to -inf and contribute exp(-inf) = 0).
+    keys j <= r + off (off from ``causal_offset``), so the keys beyond are
+    left out (every one of them would be masked to -inf and contribute
+    exp(-inf) = 0).
     """
     q = as_f64(q)
     k = as_f64(k)
@@ -112,6 +132,7 @@ def softmax_attention(q, k, v, *, causal: bool, scale: float,
     if (Bk, dk) != (B, d) or v.shape[:3] != k.shape[:3] or Hq % max(Hkv, 1):
         raise ValueError("shape mismatch")
     g = Hq // Hkv
+    off = causal_offset(Tq, Tk, align)
     O = np.zeros((B, Hq, Tq, v.shape[3]))
     L = np.full((B, Hq, Tq), _NEG_INF)
     for b in range(B):
@@ -119,17 +140,18 @@ def softmax_attention(q, k, v, *, causal: bool, scale: float,
             kh = h // g
             for r0 in range(0, Tq, row_chunk):
                 r1 = min(Tq, r0 + row_chunk)
-                kend = min(Tk, r1) if causal else Tk
+                kend = max(0, min(Tk, r1 + off)) if causal else Tk
                 rows = np.arange(r0, r1)[:, None]
                 cols = np.arange(kend)[None, :]
-                vis = (cols <= rows) if causal else np.ones((r1 - r0, kend), bool)
+                vis = (cols <= rows + off) if causal else np.ones((r1 - r0, kend), bool)
                 O[b, h, r0:r1], L[b, h, r0:r1] = _rows_three_pass(
                     q[b, h, r0:r1], k[b, kh, :kend], v[b, kh, :kend], scale, vis)
     return O, L
 
 
 def softmax_attention_rows(q, k, v, *, causal: bool, scale: float, b: int, h: int,
-                           rows: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+                           rows: Sequence[int], align: str = "top_left"
+                           ) -> Tuple[np.ndarray, np.ndarray]:
     """The same definition evaluated for selected query rows of one (b, h).
 
     Used where the full output is too large to check against one by one.
@@ -141,8 +163,9 @@ def softmax_attention_rows(q, k, v, *, causal: bool, scale: float, b: int, h: in
     Qr = as_f64(q[b, h, rows])
     K = as_f64(k[b, kh])
     V = as_f64(v[b, kh])
+    off = causal_offset(q.shape[2], K.shape[0], align)
     cols = np.arange(K.shape[0])[None, :]
-    vis = (cols <= rows[:, None]) if causal else np.ones((len(rows), K.shape[0]), bool)
+    vis = (cols <= rows[:, None] + off) if causal else np.ones((len(rows), K.shape[0]), bool)
     return _rows_three_pass(Qr, K, V, scale, vis)
 
 
@@ -150,7 +173,7 @@ def softmax_attention_rows(q, k, v, *, causal: bool, scale: float, b: int, h: in
 # Backward pass: gradients of O with respect to q, k, v
 # --------------------------------------------------------------------------
 
-def attention_backward(q, k, v, do, *, causal: bool, scale: float):
+def attention_backward(q, k, v, do, *, causal: bool, scale: float, align: str = "top_left"):
     """Gradients of the exact attention above, contracted with dO, in fp64.
 
     The plain chain rule through O = P V, P = softmax(S), S = scale * Q K^T
@@ -178,7 +201,8 @@ def attention_backward(q, k, v, do, *, causal: bool, scale: float):
     dv = np.zeros_like(v)
     rows = np.arange(Tq)[:, None]
     cols = np.arange(Tk)[None, :]
-    vis = (cols <= rows) if causal else np.ones((Tq, Tk), bool)
+    off = causal_offset(Tq, Tk, align)
+    vis = (cols <= rows + off) if causal else np.ones((Tq, Tk), bool)
     for b in range(B):
         for h in range(Hq):
             kh = h // g
@@ -202,7 +226,7 @@ def attention_backward(q, k, v, do, *, causal: bool, scale: float):
 # --------------------------------------------------------------------------
 
 def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
-                          Bc: int = 64, count: bool = False):
+                          Bc: int = 64, count: bool = False, align: str = "top_left"):
     """FlashAttention forward in fp64, FA-2 loop order.
 
     Follows [LESSON] section "Прямой проход FlashAttention" and [FUSED07]
@@ -229,6 +253,7 @@ def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
     Hkv, Tk = k.shape[1], k.shape[2]
     g = Hq // Hkv
     dv = v.shape[3]
+    off = causal_offset(Tq, Tk, align)
     O = np.zeros((B, Hq, Tq, dv))
     L = np.full((B, Hq, Tq), _NEG_INF)
     pairs = 0
@@ -244,7 +269,7 @@ def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
                 l = np.zeros(n)
                 A = np.zeros((n, dv))
                 for j0 in range(0, Tk, Bc):
-                    if causal and j0 > i_last:
+                    if causal and j0 > i_last + off:
                         break
                     pairs += 1
                     Kj = K[j0:j0 + Bc]
@@ -253,7 +278,7 @@ def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
                     if causal:
                         rows = np.arange(i0, i0 + n)[:, None]
                         cols = np.arange(j0, j0 + Kj.shape[0])[None, :]
-                        S = np.where(cols > rows, _NEG_INF, S)
+                        S = np.where(cols > rows + off, _NEG_INF, S)
                     m_new = np.maximum(m, S.max(axis=1))
                     # A row that has seen no visible key keeps m' = -inf; its
                     # sums stay zero (exp of -inf), so subtract 0 instead.

@@ -522,3 +522,138 @@ def test_backward_dv_closed_form():
     _, _, dv = oracle.attention_backward(q, k, v, np.ones((1, 1, T, d)), causal=True, scale=0.4)
     colsum = P[0, 0].sum(axis=0)
     assert np.max(np.abs(dv[0, 0] - colsum[:, None])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Bottom-right causal alignment (chunked prefill over a cache)
+# ---------------------------------------------------------------------------
+
+BR_SHAPES = [
+    # B, Hq, Hkv, Tq, Tk, d
+    (1, 4, 2, 7, 30, 8),
+    (2, 2, 2, 16, 16, 8),
+    (1, 6, 3, 1, 25, 16),
+    (1, 4, 1, 33, 70, 4),
+]
+
+
+@pytest.mark.parametrize("shape", BR_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_bottom_right_matches_torch_lower_right(shape):
+    """Library routine: torch fp64 SDPA with its lower-right causal bias."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    from torch.nn.attention.bias import causal_lower_right
+    B, Hq, Hkv, Tq, Tk, d = shape
+    rng = np.random.default_rng(31)
+    q, k, v = _rand(rng, B, Hq, Tq, d, scale=2), _rand(rng, B, Hkv, Tk, d), _rand(rng, B, Hkv, Tk, d)
+    sc = 1 / math.sqrt(d)
+    O, L = oracle.softmax_attention(q, k, v, causal=True, scale=sc, align="bottom_right")
+    g = Hq // Hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(Tq, Tk), scale=sc)
+    assert np.max(np.abs(O - ref.numpy())) < 1e-12
+    mask = causal_lower_right(Tq, Tk)._materialize()
+    s = (tq @ tk.transpose(-1, -2) * sc).masked_fill(~mask, float("-inf"))
+    assert np.max(np.abs(L - torch.logsumexp(s, dim=-1).numpy())) < 1e-12
+
+
+def test_bottom_right_equals_top_left_when_square():
+    rng = np.random.default_rng(32)
+    q, k, v = _rand(rng, 1, 2, 20, 8), _rand(rng, 1, 2, 20, 8), _rand(rng, 1, 2, 20, 8)
+    a = oracle.softmax_attention(q, k, v, causal=True, scale=0.3)
+    b = oracle.softmax_attention(q, k, v, causal=True, scale=0.3, align="bottom_right")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_bottom_right_is_the_tail_of_full_causal():
+    """A chunk of the last Tq query rows against the whole sequence's keys
+    gives the last Tq rows of the full causal (top-left) result."""
+    rng = np.random.default_rng(33)
+    T, Tq = 45, 12
+    q, k, v = _rand(rng, 1, 4, T, 8, scale=2), _rand(rng, 1, 2, T, 8), _rand(rng, 1, 2, T, 8)
+    Of, Lf = oracle.softmax_attention(q, k, v, causal=True, scale=0.35)
+    Oc, Lc = oracle.softmax_attention(q[:, :, T - Tq:], k, v, causal=True, scale=0.35,
+                                      align="bottom_right")
+    assert np.max(np.abs(Oc - Of[:, :, T - Tq:])) < 1e-14
+    assert np.max(np.abs(Lc - Lf[:, :, T - Tq:])) < 1e-14
+    dq_f, _, _ = oracle.attention_backward(q, k, v, q * 0 + 1, causal=True, scale=0.35)
+    dq_c, _, _ = oracle.attention_backward(q[:, :, T - Tq:], k, v, (q * 0 + 1)[:, :, T - Tq:],
+                                           causal=True, scale=0.35, align="bottom_right")
+    assert np.max(np.abs(dq_c - dq_f[:, :, T - Tq:])) < 1e-13
+
+
+def test_bottom_right_more_rows_than_keys():
+    """Tq > Tk: the first Tq - Tk rows see no key (O = 0, lse = -inf); row
+    Tq - Tk + i sees keys 0..i, i.e. the top-left result of the later rows."""
+    rng = np.random.default_rng(34)
+    q, k, v = _rand(rng, 1, 2, 30, 8), _rand(rng, 1, 1, 12, 8), _rand(rng, 1, 1, 12, 8)
+    O, L = oracle.softmax_attention(q, k, v, causal=True, scale=0.4, align="bottom_right")
+    assert np.all(O[:, :, :18] == 0) and np.all(L[:, :, :18] == -np.inf)
+    Ot, Lt = oracle.softmax_attention(q[:, :, 18:], k, v, causal=True, scale=0.4)
+    assert np.max(np.abs(O[:, :, 18:] - Ot)) < 1e-14 and np.max(np.abs(L[:, :, 18:] - Lt)) < 1e-14
+    Of, Lf = oracle.online_fold_attention(q, k, v, causal=True, scale=0.4, Br=7, Bc=5,
+                                          align="bottom_right")
+    assert np.max(np.abs(Of - O)) < 1e-12
+    assert np.all(Lf[:, :, :18] == -np.inf) and np.max(np.abs(Lf[:, :, 18:] - L[:, :, 18:])) < 1e-12
+
+
+@pytest.mark.parametrize("Br,Bc", [(64, 64), (7, 13), (1, 1)])
+def test_bottom_right_fold_and_rows_match_three_pass(Br, Bc):
+    rng = np.random.default_rng(35)
+    q, k, v = _rand(rng, 1, 4, 37, 16, scale=3), _rand(rng, 1, 2, 90, 16), _rand(rng, 1, 2, 90, 16)
+    O, L = oracle.softmax_attention(q, k, v, causal=True, scale=0.25, align="bottom_right")
+    Of, Lf, pairs = oracle.online_fold_attention(q, k, v, causal=True, scale=0.25, Br=Br, Bc=Bc,
+                                                 count=True, align="bottom_right")
+    assert np.max(np.abs(O - Of)) < 1e-12 and np.max(np.abs(L - Lf)) < 1e-12
+    rows = [0, 5, 36]
+    Or, Lr = oracle.softmax_attention_rows(q, k, v, causal=True, scale=0.25, b=0, h=3, rows=rows,
+                                           align="bottom_right")
+    assert np.max(np.abs(Or - O[0, 3, rows])) < 1e-14 and np.max(np.abs(Lr - L[0, 3, rows])) < 1e-14
+
+
+def test_decode_is_bottom_right_single_row():
+    """One new token over a cache of n keys is bottom-right attention with
+    Tq = 1 (it sees every cached key)."""
+    q, kc, vc, sl = _small_decode(poison=False)
+    O, L = oracle.decode_attention(q, kc, vc, sl)
+    d = q.shape[-1]
+    for b in range(q.shape[0]):
+        n = sl[b]
+        Op, Lp = oracle.softmax_attention(q[b:b + 1, :, None, :], kc[b:b + 1, :, :n],
+                                          vc[b:b + 1, :, :n], causal=True, scale=1 / math.sqrt(d),
+                                          align="bottom_right")
+        assert np.max(np.abs(O[b] - Op[0, :, 0])) < 1e-14
+        assert np.max(np.abs(L[b] - Lp[0, :, 0])) < 1e-14
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 7, 19, 8), (1, 2, 1, 13, 13, 4)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_bottom_right_matches_torch_autograd(shape):
+    torch = pytest.importorskip("torch")
+    from torch.nn.attention.bias import causal_lower_right
+    B, Hq, Hkv, Tq, Tk, d = shape
+    rng = np.random.default_rng(36)
+    q, k, v, do = (_rand(rng, B, Hq, Tq, d), _rand(rng, B, Hkv, Tk, d),
+                   _rand(rng, B, Hkv, Tk, d), _rand(rng, B, Hq, Tq, d))
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    g = Hq // Hkv
+    S = scale * (tq @ tk.repeat_interleave(g, dim=1).transpose(-1, -2))
+    S = S.masked_fill(~causal_lower_right(Tq, Tk)._materialize(), float("-inf"))
+    O = torch.softmax(S, dim=-1) @ tv.repeat_interleave(g, dim=1)
+    O.backward(torch.tensor(do))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, causal=True, scale=scale,
+                                           align="bottom_right")
+    assert np.max(np.abs(dq - tq.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dk - tk.grad.numpy())) < 1e-12
+    assert np.max(np.abs(dv - tv.grad.numpy())) < 1e-12
+
+
+def test_causal_offset_values():
+    assert oracle.causal_offset(5, 9, "top_left") == 0
+    assert oracle.causal_offset(5, 9, "bottom_right") == 4
+    assert oracle.causal_offset(9, 5, "bottom_right") == -4
+    with pytest.raises(ValueError):
+        oracle.causal_offset(1, 1, "middle")
