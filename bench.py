@@ -124,7 +124,7 @@ def prefill_case(torch, fa, w, steps, warmup, seed=0):
     stream = torch.cuda.current_stream()
 
     launch = fa.prepared("fa_fwd", q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d,
-                         int(w.causal), w.scale, stream=stream)
+                         w.causal_mode, w.scale, stream=stream)
     wall, ev_ms = time_calls(torch, launch, steps, warmup)
     del q, k, v, o, lse
     return wall, ev_ms
@@ -143,10 +143,10 @@ def backward_case(torch, fa, w, steps, warmup, seed=0):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.causal, w.scale, stream)
+    fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d, w.causal_mode, w.scale, stream)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     launch = fa.prepared("fa_bwd", q, k, v, o, lse, do, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Tq,
-                         w.Tk, w.d, int(w.causal), w.scale, stream=stream)
+                         w.Tk, w.d, w.causal_mode, w.scale, stream=stream)
     wall, ev_ms = time_calls(torch, launch, steps, warmup)
     del q, k, v, do, o, lse, dq, dk, dv
     return wall, ev_ms
@@ -339,7 +339,8 @@ def main():
 
     if not args.no_extra:
         also = {}
-        for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 10)):
+        for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 10),
+                            ("llama3_8b_chunk", 20)):
             wk = inputs.WORKLOADS[name]
             log(f"[bench] {wk.name}")
             wl, ev = prefill_case(torch, fa, wk, steps, max(2, min(args.warmup, steps)))

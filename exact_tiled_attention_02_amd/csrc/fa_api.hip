@@ -50,8 +50,9 @@ int workspace(hipStream_t stream, size_t need, char** out) {
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const void* o, int B, int Hq, int Hkv,
-              int Tq, int Tk, int d, float scale, bool* empty) {
+              int Tq, int Tk, int d, int causal, float scale, bool* empty) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_SHAPE;
+  if (causal < 0 || causal > 2) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -69,8 +70,12 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
   return FA_OK;
 }
 
+// Causal offset: row i sees key j iff j <= i + offset (1: top-left, 2:
+// bottom-right).
+int causal_offset(int causal, int Tq, int Tk) { return causal == 2 ? Tk - Tq : 0; }
+
 fa::FwdParams make_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                       int Hq, int Hkv, int Tq, int Tk, int d, float scale) {
+                       int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale) {
   fa::FwdParams p{};
   p.q = q;
   p.k = k;
@@ -91,6 +96,7 @@ fa::FwdParams make_fwd(const void* q, const void* k, const void* v, void* o, flo
   const double a = fabs((double)scale);
   p.c = (float)(fmax(a, 1e-30) * 1.4426950408889634);
   p.negate_q = scale < 0.f ? 1 : 0;
+  p.causal_off = causal_offset(causal, Tq, Tk);
   (void)d;
   return p;
 }
@@ -142,18 +148,18 @@ extern "C" {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Tq, int Tk, int d, int causal, float scale, void* stream) {
   bool empty = false;
-  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, scale, &empty);
+  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, causal, scale, &empty);
   if (st != FA_OK || empty) return st;
-  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale);
+  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale);
   return map_err(fa::launch_fwd_bf16(p, d, causal != 0, (hipStream_t)stream));
 }
 
 int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq,
                int Hkv, int Tq, int Tk, int d, int causal, float scale, void* stream) {
   bool empty = false;
-  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, scale, &empty);
+  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, causal, scale, &empty);
   if (st != FA_OK || empty) return st;
-  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, scale);
+  const fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale);
   return map_err(fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
 }
 
@@ -161,6 +167,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk,
            int d, int causal, float scale, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tq < 0 || Tk < 0) return FA_ERR_SHAPE;
+  if (causal < 0 || causal > 2) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (!isfinite(scale)) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -201,6 +208,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.Tq = Tq;
   p.Tk = Tk;
   p.Tqp = (int)Tqp;
+  p.causal_off = causal_offset(causal, Tq, Tk);
   p.g = Hq / Hkv;
   p.c = (float)((double)scale * 1.4426950408889634);
   p.scale = scale;

@@ -31,14 +31,16 @@
 //     32 query rows a wavefront forms S = Q K^T and dP = dO V^T (lane = key,
 //     registers = queries), P and dS in registers, then dV^T += dO^T P and
 //     dK^T += Q^T dS with dO^T and Q^T read through the transposing LDS read.
-//     Under the causal mask the query rows before the workgroup's first key
-//     are never visited and 32x32 blocks above the diagonal are skipped.
+//     Under the causal mask the query rows that see none of the workgroup's
+//     keys are never visited and 32x32 blocks above the diagonal are skipped.
 //  3. bwd_dq: a workgroup owns 32*NW query rows of one query head; Q and dO
 //     stay in registers and dQ^T in accumulators while tiles of 64 keys (K,
 //     V) stream through LDS.  Per 32 keys: S^T = K Q^T and dP^T = V dO^T
 //     (lane = query), P^T and dS^T, then dQ^T += K^T dS^T with K^T read
-//     transposed.  Key tiles after the workgroup's last row are never
+//     transposed.  Key tiles after the workgroup's last row's limit are never
 //     visited under the causal mask.
+// The causal diagonal is top-left (row i sees keys j <= i) or bottom-right
+// (j <= i + Tk - Tq, a chunk of queries at the end of a cached sequence).
 // The probabilities and dS are rounded to bf16 for the matrix products that
 // consume them; all sums are fp32.  Masked entries of P are set to 0
 // explicitly (never through -inf), so any finite scale works.
@@ -247,8 +249,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       dk[i][r] = 0.f;
     }
 
-  // Query tiles: rows qs .. Tq-1 of each of the g query heads.
-  const int qs = CAUSAL ? k0 : 0;
+  // Query tiles: rows qs .. Tq-1 of each of the g query heads.  Causal: row i
+  // sees key j iff j <= i + off, so rows before k0 - off see none of these
+  // keys (qs is kept a multiple of the tile height).
+  const int off = p.causal_off;
+  const int qs = CAUSAL ? max(0, k0 - off) / kQTile * kQTile : 0;
   const int ntq = qs < p.Tq ? (p.Tq - qs + kQTile - 1) / kQTile : 0;
   const int nit = p.g * ntq;
 
@@ -337,7 +342,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
       // Row offsets 8*(r/4) + r%4 outside [lo, hi) are masked: rows past
       // Tq, and under the causal mask rows before this lane's key.
       const int base = q0h + 4 * half;
-      const int lo = CAUSAL ? my_k - base : -64;
+      const int lo = CAUSAL ? my_k - off - base : -64;
       const int hi = p.Tq - base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -406,11 +411,11 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     const int q0 = qs + (it % ntq) * kQTile;
     static_for<0, 2>([&](auto hf_c) {
       const int q0h = q0 + 32 * hf_c;
-      // Under the causal mask query i sees key j iff j <= i; kw and q0h are
-      // multiples of 32.  Blocks with every key after every row are skipped;
-      // only the diagonal block and the last rows need the mask.
-      if (CAUSAL && q0h < kw) return;
-      const bool mask = (CAUSAL && q0h == kw) || q0h + 32 > p.Tq;
+      // Under the causal mask query i sees key j iff j <= i + off.  Blocks
+      // with every key after every row's limit are skipped; only blocks that
+      // cross the diagonal and the last rows need the mask.
+      if (CAUSAL && q0h + 31 + off < kw) return;
+      const bool mask = (CAUSAL && q0h + off < kw + 31) || q0h + 32 > p.Tq;
       if constexpr (D == 128)
         rows32(q0h, st_c, hf_c, IC<2>{}, mask);
       else if (mask)
@@ -484,10 +489,13 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[i][r] = 0.f;
 
-  const int kend = CAUSAL ? min(p.Tk, q_end) : p.Tk;
+  const int off = p.causal_off;   // causal: row i sees key j iff j <= i + off
+  const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
   const int ntiles = (kend + kKTile - 1) / kKTile;
   // Key tiles this wavefront computes: none past its own last row.
-  const int my_tiles = q0w >= p.Tq ? 0 : CAUSAL ? min(ntiles, (q0w + 31) / kKTile + 1) : ntiles;
+  const int my_tiles = q0w >= p.Tq ? 0
+                       : CAUSAL ? (q0w + 31 + off < 0 ? 0 : min(ntiles, (q0w + 31 + off) / kKTile + 1))
+                                : ntiles;
 
   uint32_t csrc[NCOPY];
 #pragma unroll
@@ -557,7 +565,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_dq_kernel(const BwdParams p) {
       // Key offsets 8*(r/4) + r%4 at or past hi are masked: keys past Tk,
       // and under the causal mask keys after this lane's row.
       const int base = kb0 + 4 * half;
-      const int hi = CAUSAL ? min(p.Tk, my_q + 1) - base : p.Tk - base;
+      const int hi = CAUSAL ? max(0, min(p.Tk, my_q + off + 1)) - base : p.Tk - base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
@@ -599,8 +607,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_dq_kernel(const BwdParams p) {
     if (t < my_tiles) {
       static_for<0, 2>([&](auto kb_c) {
         const int kb0 = t * kKTile + 32 * kb_c;
-        if (CAUSAL && kb0 > q0w + 31) return;   // every key after every row
-        const bool mask = kb0 + 32 > p.Tk || (CAUSAL && kb0 + 31 > q0w);
+        if (CAUSAL && kb0 > q0w + 31 + off) return;   // every key after every row's limit
+        const bool mask = kb0 + 32 > p.Tk || (CAUSAL && kb0 + 31 > q0w + off);
         if constexpr (D == 128)
           keys32(kb0, st_c, kb_c, IC<2>{}, mask);
         else if (mask)

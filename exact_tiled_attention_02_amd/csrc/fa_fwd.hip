@@ -41,7 +41,9 @@
 //    over banks).
 //  * Causal: key tiles starting after the workgroup's last row are never
 //    visited; only tiles crossing the diagonal (or the key tail) are masked,
-//    with -inf before the max ([FUSED07] task 07.2 pitfalls).  A workgroup
+//    with -inf before the max ([FUSED07] task 07.2 pitfalls).  The diagonal
+//    is top-left (row i sees keys j <= i) or, for a chunk of queries at the
+//    end of a cached sequence, bottom-right (j <= i + Tk - Tq).  A workgroup
 //    pairs a light and the mirrored heavy half-tile of query rows so that
 //    all workgroups carry the same work.
 #include <type_traits>
@@ -187,12 +189,19 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     }
   }
 
-  // Keys this workgroup needs: all, or under the causal mask those at or
-  // before its last (real) query row.
-  const int kend = CAUSAL ? min(p.Tk, q_end) : p.Tk;
+  // Causal: row i sees key j iff j <= i + off (off = 0 top-left, Tk - Tq
+  // bottom-right).  Keys this workgroup needs: all, or under the causal mask
+  // those at or before its last (real) query row's limit.
+  const int off = p.causal_off;
+  const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
   const int ntiles = (kend + kBN - 1) / kBN;
   // Last key tile this wavefront computes (its rows see no key after it).
-  const int my_tiles = !active ? 0 : CAUSAL ? min(ntiles, (q0w + 31) / kBN + 1) : ntiles;
+  const int my_tiles = !active ? 0
+                       : CAUSAL ? (q0w + 31 + off < 0 ? 0 : min(ntiles, (q0w + 31 + off) / kBN + 1))
+                                : ntiles;
+  // A row that sees no key at all (bottom-right with Tq > Tk) keeps m = -inf;
+  // its rescale factor is 1 and its exponent offset 0, so it stays at 0.
+  const bool has_keys = !CAUSAL || my_q + off >= 0;
 
   // Global->LDS copies through buffer resources covering this head's K and
   // V: reads past the last key return zeros (finite; those keys are masked).
@@ -307,14 +316,14 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
     // Mask (only tiles that cross the diagonal or the key tail): -inf
     // before the max, so masked keys get probability exactly 0.
-    const bool need_mask = (t0 + kBN > p.Tk) || (CAUSAL && t0 + kBN - 1 > q0w);
+    const bool need_mask = (t0 + kBN > p.Tk) || (CAUSAL && t0 + kBN - 1 > q0w + off);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q);
+          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
           s[kb][r] = vis ? s[kb][r] : kNegInf;
         }
     }
@@ -332,14 +341,14 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     // "FlashAttention-2": rescale only if the maximum increased); l always
     // takes its factor (exactly 1 where the max did not move).
     const float m_new = fmaxf(m, mt);
-    const float corr = exp2_fast((m - m_new) * c);
+    const float corr = has_keys ? exp2_fast((m - m_new) * c) : 1.f;
     if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
 #pragma unroll
       for (int i = 0; i < ND; ++i) acc[i] *= corr;
     }
     l *= corr;
     m = m_new;
-    const float mc = m * c;
+    const float mc = has_keys ? m * c : 0.f;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -465,8 +474,10 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
     qf[i] = my_q < p.Tq ? sgn * Qg[(size_t)my_q * D + 2 * i + half] : 0.f;
 
   const int q_last = min(p.Tq, q0 + 128);
-  const int kend = CAUSAL ? min(p.Tk, q_last) : p.Tk;
+  const int off = p.causal_off;   // causal: row i sees key j iff j <= i + off
+  const int kend = CAUSAL ? max(0, min(p.Tk, q_last + off)) : p.Tk;
   const int ntiles = (kend + BN - 1) / BN;
+  const bool has_keys = !CAUSAL || my_q + off >= 0;
 
   const float c = p.c;
   float m = kNegInf, l = 0.f;
@@ -489,7 +500,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
     }
     __syncthreads();
 
-    const bool act = !CAUSAL || t0 <= q0w + 31;
+    const bool act = !CAUSAL || t0 <= q0w + 31 + off;
     if (!act) continue;
     f32x16 s;
 #pragma unroll
@@ -497,12 +508,12 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
 #pragma unroll
     for (int i = 0; i < D / 2; ++i) s = mma_32x32x2_f32(Ks[col * KS + 2 * i + half], qf[i], s);
 
-    const bool need_mask = (t0 + BN > p.Tk) || (CAUSAL && t0 + BN - 1 > q0w);
+    const bool need_mask = (t0 + BN > p.Tk) || (CAUSAL && t0 + BN - 1 > q0w + off);
     if (need_mask) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = key < p.Tk && (!CAUSAL || key <= my_q);
+        const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
         s[r] = vis ? s[r] : kNegInf;
       }
     }
@@ -511,8 +522,8 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
     for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
     mt = fmaxf(mt, swap_halves(mt));
     const float m_new = fmaxf(m, mt);
-    const float corr = exp2_fast((m - m_new) * c);
-    const float mc = m_new * c;
+    const float corr = has_keys ? exp2_fast((m - m_new) * c) : 1.f;
+    const float mc = has_keys ? m_new * c : 0.f;
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

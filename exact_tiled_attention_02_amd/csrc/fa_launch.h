@@ -17,6 +17,7 @@ struct FwdParams {
   float c;         // |scale| * log2(e), the factor that turns scores into base-2 exponents
   int negate_q;    // scale < 0: queries are sign-flipped on load, c uses |scale|
   int pair;        // causal: workgroups pair mirrored light/heavy half-tiles
+  int causal_off;  // causal: row i sees key j iff j <= i + causal_off (0 or Tk - Tq)
 };
 
 // One decode call.  q,o: [B,Hq,d]; caches: [B,Hkv,Tk_max,d].
@@ -58,6 +59,7 @@ struct BwdParams {
   float* l2;         // lse * log2(e) per query row; 0 on padding rows
   float* delta;      // dO_i . O_i per query row; 0 on padding rows
   int B, Hq, Hkv, Tq, Tk;
+  int causal_off;    // causal: row i sees key j iff j <= i + causal_off
   int Tqp;           // Tq rounded up to a multiple of kBwdRowPad
   int g;             // Hq / Hkv
   float c;           // scale * log2(e) (signed)

@@ -97,20 +97,31 @@ def _check(st: int, where: str) -> None:
 
 # --- one-to-one entry points -------------------------------------------------
 
+def _causal(c) -> int:
+    """0 / False: no mask; 1 / True: top-left causal; 2: bottom-right causal."""
+    if isinstance(c, bool):
+        return int(c)
+    if c == "bottom_right":
+        return 2
+    if c == "top_left":
+        return 1
+    return int(c)
+
+
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
     _check(load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d,
-                         int(bool(causal)), float(scale), _stream(stream)), "fa_fwd")
+                         _causal(causal), float(scale), _stream(stream)), "fa_fwd")
 
 
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
     _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk,
-                             d, int(bool(causal)), float(scale), _stream(stream)), "fa_fwd_f32")
+                             d, _causal(causal), float(scale), _stream(stream)), "fa_fwd_f32")
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale,
            stream=None) -> None:
     _check(load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                         _ptr(dk), _ptr(dv), B, Hq, Hkv, Tq, Tk, d, int(bool(causal)),
+                         _ptr(dk), _ptr(dv), B, Hq, Hkv, Tq, Tk, d, _causal(causal),
                          float(scale), _stream(stream)), "fa_bwd")
 
 

@@ -69,16 +69,30 @@ class Prefill:
     dtype: str = "bf16"          # "bf16" or "f32"
     q_mult: float = 1.0
     seed: int = 0
+    align: str = "top_left"      # causal diagonal: "top_left" or "bottom_right"
 
     @property
     def scale(self) -> float:
         return 1.0 / float(np.sqrt(self.d))
 
     @property
+    def causal_mode(self) -> int:
+        """The C ABI's causal argument: 0 none, 1 top-left, 2 bottom-right."""
+        if not self.causal:
+            return 0
+        return 2 if self.align == "bottom_right" else 1
+
+    @property
     def flops(self) -> float:
-        """Attention FLOPs, 4*B*Hq*Tq*Tk*d, halved for causal."""
+        """Attention FLOPs, 4*B*Hq*Tq*Tk*d, halved for causal.  For a
+        bottom-right chunk (Tq < Tk) the Tk - Tq cached keys are seen by every
+        row and the square part is halved: 4*B*Hq*d*Tq*(Tk - Tq + Tq/2)."""
         f = 4.0 * self.B * self.Hq * self.Tq * self.Tk * self.d
-        return f / 2 if self.causal else f
+        if not self.causal:
+            return f
+        if self.align == "bottom_right" and self.Tk > self.Tq:
+            return 4.0 * self.B * self.Hq * self.d * self.Tq * (self.Tk - self.Tq + self.Tq / 2)
+        return f / 2
 
     @property
     def bwd_flops(self) -> float:
@@ -118,7 +132,8 @@ class Decode:
         return 1.0 / float(np.sqrt(self.d))
 
 
-# The five workloads the pages' hot path is measured on.
+# The five workloads the pages' hot path is measured on, and a chunked-prefill
+# workload for the bottom-right causal alignment.
 SINGLE_HEAD_F32 = Prefill("single-head fp32 attention, T=256, d=64, non-causal",
                           B=1, Hq=1, Hkv=1, Tq=256, Tk=256, d=64, causal=False,
                           dtype="f32")
@@ -129,6 +144,10 @@ QWEN3_0P6B_GQA = Prefill("Qwen3-0.6B GQA causal prefill, Hq=16, Hkv=8, T=4096, d
                          q_mult=3.0)
 LLAMA3_8B_LONG = Prefill("Llama-3-8B GQA causal prefill, Hq=32, Hkv=8, T=32768, d=128",
                          B=1, Hq=32, Hkv=8, Tq=32768, Tk=32768, d=128, causal=True)
+LLAMA3_8B_CHUNK = Prefill("Llama-3-8B GQA chunked prefill, last 4096 of 32768 positions "
+                          "(bottom-right causal), Hq=32, Hkv=8, d=128",
+                          B=1, Hq=32, Hkv=8, Tq=4096, Tk=32768, d=128, causal=True,
+                          align="bottom_right")
 FLASH_DECODE = Decode("split-KV decode, B=16, Hq=32, Hkv=8, d=128, seqlen U[1024,32768]",
                       B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768)
 
@@ -137,6 +156,7 @@ WORKLOADS = {
     "gpt2_small_mha": GPT2_SMALL_MHA,
     "qwen3_0p6b_gqa": QWEN3_0P6B_GQA,
     "llama3_8b_long": LLAMA3_8B_LONG,
+    "llama3_8b_chunk": LLAMA3_8B_CHUNK,
     "flash_decode": FLASH_DECODE,
 }
 

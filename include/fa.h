@@ -56,8 +56,17 @@ typedef enum {
  *     s_ij   = scale * <q[b,hq,i,:], k[b,kh,j,:]>,   kh = hq / (Hq / Hkv)
  *     o[b,hq,i,:] = sum_j softmax_j(s_ij) * v[b,kh,j,:]
  *     lse[b,hq,i] = log sum_j exp(s_ij)              (natural log)
- * over the keys j visible to row i: all j < Tk, or with causal != 0 only
- * j <= i (top-left alignment when Tq != Tk).  This is softmax(Q K^T * scale) V
+ * over the keys j visible to row i:
+ *     causal == 0   all j < Tk;
+ *     causal == 1   j <= i (top-left alignment, the reference mask of
+ *                   [FUSED07] section "FlashAttention-наив на numpy");
+ *     causal == 2   j <= i + Tk - Tq (bottom-right alignment: the Tq queries
+ *                   are the last Tq positions of a sequence whose first
+ *                   Tk - Tq positions are already cached, i.e. chunked
+ *                   prefill; Tq = 1 is the decode rule of [NOTE] section
+ *                   "Prefill i dekodowanie to różne problemy").  With
+ *                   Tq > Tk the first Tq - Tk rows see no key.
+ * Rows that see no key get o = 0 and lse = -inf.  This is softmax(Q K^T * scale) V
  * computed tile by tile with the online softmax of [FUSED07] section
  * "Online softmax: вывод" and the forward pass of [LESSON] section
  * "Прямой проход FlashAttention"; neither the score matrix nor the
@@ -76,8 +85,8 @@ typedef enum {
  * probabilities are rounded to bf16 before the p.v product.
  * B == 0, Hq == 0 or Tq == 0 is a valid empty call.  Tk == 0 gives o = 0 and
  * lse = -inf.  Errors: FA_ERR_NULL (q, k, v or o NULL on a non-empty call),
- * FA_ERR_SHAPE (negative sizes, Hkv < 1, Hq % Hkv != 0, non-finite scale),
- * FA_ERR_UNSUPPORTED (d not 64/128), FA_ERR_LAUNCH.
+ * FA_ERR_SHAPE (negative sizes, Hkv < 1, Hq % Hkv != 0, non-finite scale,
+ * causal outside 0..2), FA_ERR_UNSUPPORTED (d not 64/128), FA_ERR_LAUNCH.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Tq, int Tk, int d, int causal, float scale,
@@ -105,7 +114,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *     dv_j = sum_i P_ij dout_i,          dP_ij = dout_i . v_j,
  *     dS_ij = P_ij (dP_ij - D_i),
  *     dq_i = scale * sum_j dS_ij k_j,    dk_j = scale * sum_i dS_ij q_i,
- * over the (i, j) pairs visible under the same mask as fa_fwd.  With
+ * over the (i, j) pairs visible under the same mask as fa_fwd (causal 0, 1
+ * or 2 as there).  With
  * grouped-query attention ([NOTE] section "Prefill i dekodowanie to różne
  * problemy") dk and dv of kv head kh sum the contributions of its g = Hq/Hkv
  * query heads.  Nothing of size Tq x Tk is stored.
@@ -128,7 +138,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * dk = dv = 0 (q, o, lse, dout and dq may then be NULL); Tk == 0 gives
  * dq = 0 (k, v, dk and dv may then be NULL).  Errors: FA_ERR_NULL,
  * FA_ERR_SHAPE (negative sizes, Hkv < 1, Hq % Hkv != 0, non-finite scale,
- * sizes whose workgroup counts overflow), FA_ERR_UNSUPPORTED (d not 64/128),
+ * causal outside 0..2, sizes whose workgroup counts overflow),
+ * FA_ERR_UNSUPPORTED (d not 64/128),
  * FA_ERR_ALLOC, FA_ERR_DEVICE, FA_ERR_LAUNCH.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -60,7 +60,8 @@ BF16_U = 2.0 ** -8    # unit roundoff of bf16 (8 significant bits, nearest even)
 F32_U = 2.0 ** -24
 
 
-def bwd_error_bounds(q, k, v, do, O, L, o_used, lse_used, *, causal, scale, safety=1.25):
+def bwd_error_bounds(q, k, v, do, O, L, o_used, lse_used, *, causal, scale, safety=1.25,
+                     causal_off=0):
     """First-order bounds on |kernel - exact| for dq, dk, dv, element by element.
 
     Inputs are fp64 [B,H,T,d] arrays: q, k, v, do as the kernel received them
@@ -94,17 +95,20 @@ def bwd_error_bounds(q, k, v, do, O, L, o_used, lse_used, *, causal, scale, safe
         return bdq, bdk, bdv
     i_idx = np.arange(Tq)[:, None]
     j_idx = np.arange(Tk)[None, :]
-    vis = (j_idx <= i_idx) if causal else np.ones((Tq, Tk), bool)
+    vis = (j_idx <= i_idx + causal_off) if causal else np.ones((Tq, Tk), bool)
     for b in range(B):
         for h in range(Hq):
             kh = h // g
             s = scale * (q[b, h] @ k[b, kh].T)
-            P = np.where(vis, np.exp(np.where(vis, s, 0.0) - L[b, h][:, None]), 0.0)
+            Lf = np.where(np.isfinite(L[b, h]), L[b, h], 0.0)
+            P = np.where(vis, np.exp(np.where(vis, s, 0.0) - Lf[:, None]), 0.0)
             dP = do[b, h] @ v[b, kh].T
             D = np.sum(do[b, h] * O[b, h], axis=1)
             dS = P * (dP - D[:, None])
             smax = np.max(np.where(vis, np.abs(s), 0.0), axis=1)
-            rho = np.expm1(np.abs(lse_used[b, h] - L[b, h])) + 2.0 ** -21 * (smax + np.abs(L[b, h]) + 1)
+            has = np.isfinite(L[b, h])   # rows with no visible key have P = 0
+            dlse = np.where(has, np.abs(np.where(has, lse_used[b, h], 0) - np.where(has, L[b, h], 0)), 0)
+            rho = np.expm1(dlse) + 2.0 ** -21 * (smax + np.where(has, np.abs(L[b, h]), 0) + 1)
             dD = (np.sum(np.abs(do[b, h]) * np.abs(o_used[b, h] - O[b, h]), axis=1) +
                   2.0 ** -20 * np.sum(np.abs(do[b, h] * O[b, h]), axis=1))
             edS = gam * np.abs(dS) + rho[:, None] * P * np.abs(dP - D[:, None]) + P * dD[:, None]

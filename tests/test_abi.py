@@ -59,6 +59,8 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
     ((P, P, P, P, P, 0, 4, 2, 8, 8, 64, 1, 0.1), 0),                  # empty batch: no-op
     ((P, P, P, P, P, 2, 4, 2, 0, 8, 64, 0, 0.1), 0),                  # no query rows: no-op
     ((FAKE, FAKE, FAKE, FAKE, P, 1, 1, 1, 65535 * 32 + 1, 8, 64, 1, 0.1), 2),  # too many rows
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, 3, 0.1), 2),      # causal mode 3
+    ((FAKE, FAKE, FAKE, FAKE, P, 1, 4, 2, 8, 8, 64, -1, 0.1), 2),     # causal mode -1
 ])
 @pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_f32"])
 def test_fwd_validation(lib, entry, args, status):
@@ -75,6 +77,7 @@ def test_fwd_validation(lib, entry, args, status):
     ((FAKE,) * 9 + (1, 4, 2, -1, 8, 64, 1, 0.1), 2),                # negative Tq
     ((FAKE,) * 9 + (1, 4, 2, 8, -1, 64, 1, 0.1), 2),                # negative Tk
     ((FAKE,) * 9 + (1, 4, 2, 8, 8, 64, 1, float("nan")), 2),
+    ((FAKE,) * 9 + (1, 4, 2, 8, 8, 64, 3, 0.1), 2),                 # causal mode 3
     ((FAKE,) * 4 + (P,) + (FAKE,) * 4 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # lse NULL
     ((FAKE,) * 5 + (P,) + (FAKE,) * 3 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # dout NULL
     ((FAKE,) * 6 + (P,) + (FAKE,) * 2 + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # dq NULL

@@ -50,19 +50,21 @@ def run_bwd(q, k, v, o_bits, lse32, do, causal, scale):
     return host_bf16_as_f64(dq), host_bf16_as_f64(dk), host_bf16_as_f64(dv)
 
 
-def parity(w: inputs.Prefill, scale=None):
+def parity(w: inputs.Prefill, scale=None, align="top_left"):
     causal = w.causal
     sc = w.scale if scale is None else scale
     q, k, v, do = inputs.prefill_inputs_with_grad(w)
-    O, L = oracle.softmax_attention(q, k, v, causal=causal, scale=sc)
+    O, L = oracle.softmax_attention(q, k, v, causal=causal, scale=sc, align=align)
     o_bits = to_bf16_bits(O)
     lse32 = L.astype(np.float32)
-    say("fa_bwd", w)
-    dq, dk, dv = run_bwd(q, k, v, o_bits, lse32, do, causal, sc)
-    rq, rk, rv = oracle.attention_backward(q, k, v, do, causal=causal, scale=sc)
+    say("fa_bwd", w, align)
+    mode = (2 if align == "bottom_right" else 1) if causal else 0
+    dq, dk, dv = run_bwd(q, k, v, o_bits, lse32, do, mode, sc)
+    rq, rk, rv = oracle.attention_backward(q, k, v, do, causal=causal, scale=sc, align=align)
     bq, bk, bv = bwd_error_bounds(oracle.as_f64(q), oracle.as_f64(k), oracle.as_f64(v),
                                   oracle.as_f64(do), O, L, oracle.as_f64(o_bits),
-                                  lse32.astype(np.float64), causal=causal, scale=sc)
+                                  lse32.astype(np.float64), causal=causal, scale=sc,
+                                  causal_off=oracle.causal_offset(w.Tq, w.Tk, align))
     check_bounded("dq", dq, rq, bq)
     check_bounded("dk", dk, rk, bk)
     check_bounded("dv", dv, rv, bv)
@@ -94,6 +96,26 @@ SMALL = [
 def test_bwd_small_shapes(shape):
     B, Hq, Hkv, Tq, Tk, d, causal = shape
     parity(inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=causal, seed=11))
+
+
+BOTTOM_RIGHT = [
+    # B, Hq, Hkv, Tq, Tk, d
+    (1, 4, 2, 70, 300, 128),
+    (1, 2, 1, 1, 257, 64),
+    (2, 4, 4, 100, 100, 64),
+    (1, 8, 2, 129, 1000, 64),
+    (1, 2, 2, 200, 65, 128),     # Tq > Tk: the first 135 rows see no key
+    (1, 6, 3, 33, 97, 128),
+]
+
+
+@pytest.mark.parametrize("shape", BOTTOM_RIGHT, ids=lambda s: "x".join(map(str, s)))
+def test_bwd_bottom_right(shape):
+    B, Hq, Hkv, Tq, Tk, d = shape
+    dq, _, _ = parity(inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=True,
+                                     seed=18), align="bottom_right")
+    if Tq > Tk:
+        assert np.all(dq[:, :, :Tq - Tk] == 0)
 
 
 def test_bwd_keys_past_last_row_get_zero():

@@ -98,6 +98,79 @@ def test_f32_small_shapes(shape):
     check("lse", L, Lr, F32_TOL)
 
 
+BOTTOM_RIGHT = [
+    # B, Hq, Hkv, Tq, Tk, d
+    (1, 4, 2, 70, 300, 128),
+    (1, 2, 1, 1, 257, 64),
+    (2, 4, 4, 100, 100, 64),
+    (1, 8, 2, 129, 1000, 64),
+    (1, 2, 2, 200, 65, 128),     # Tq > Tk: the first 135 rows see no key
+    (1, 6, 3, 33, 97, 128),
+    (1, 16, 4, 700, 2100, 128),  # a grid small enough for paired half-tiles
+]
+
+
+@pytest.mark.parametrize("shape", BOTTOM_RIGHT, ids=lambda s: "x".join(map(str, s)))
+def test_bf16_bottom_right(shape):
+    from exact_tiled_attention_02_amd import fa
+    B, Hq, Hkv, Tq, Tk, d = shape
+    w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=True, seed=19)
+    q, k, v = inputs.prefill_inputs(w)
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o = torch.full((B, Hq, Tq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    say("fa_fwd bf16 bottom-right", shape)
+    fa.fa_fwd(tq, tk, tv, o, lse, B, Hq, Hkv, Tq, Tk, d, 2, w.scale, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    O, L = host_bf16_as_f64(o), host_f64(lse)
+    Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale, align="bottom_right")
+    check("O", O, Or, BF16_O_TOL)
+    check("lse", L, Lr, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("shape", BOTTOM_RIGHT[:6], ids=lambda s: "x".join(map(str, s)))
+def test_f32_bottom_right(shape):
+    from exact_tiled_attention_02_amd import fa
+    B, Hq, Hkv, Tq, Tk, d = shape
+    w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=True, dtype="f32",
+                       seed=20)
+    q, k, v = inputs.prefill_inputs(w)
+    tq, tk, tv = dev_f32(q), dev_f32(k), dev_f32(v)
+    o = torch.full((B, Hq, Tq, d), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    say("fa_fwd_f32 bottom-right", shape)
+    fa.fa_fwd_f32(tq, tk, tv, o, lse, B, Hq, Hkv, Tq, Tk, d, 2, w.scale,
+                  torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale, align="bottom_right")
+    check("O", host_f64(o), Or, F32_TOL)
+    check("lse", host_f64(lse), Lr, F32_TOL)
+
+
+def test_bottom_right_chunk_of_llama3_long_sampled():
+    """Chunked prefill at full size: the last 4096 positions of a 32768-token
+    Llama-3-shaped sequence (Hq=32, Hkv=8, d=128) against all 32768 cached
+    keys; sampled rows of a spread of heads checked one by one."""
+    from exact_tiled_attention_02_amd import fa
+    w = inputs.Prefill("t", B=1, Hq=32, Hkv=8, Tq=4096, Tk=32768, d=128, causal=True, seed=21)
+    q, k, v = inputs.prefill_inputs(w)
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    o = torch.empty((1, 32, 4096, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((1, 32, 4096), dtype=torch.float32, device="cuda")
+    say("fa_fwd bf16 bottom-right chunk 4096 of 32768")
+    fa.fa_fwd(tq, tk, tv, o, lse, 1, 32, 8, 4096, 32768, 128, 2, w.scale,
+              torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    O, L = host_bf16_as_f64(o), host_f64(lse)
+    rng = np.random.default_rng(5)
+    for h in (0, 13, 31):
+        rows = _sample_rows(4096, rng, n_random=64)
+        Or, Lr = oracle.softmax_attention_rows(q, k, v, causal=True, scale=w.scale, b=0, h=h,
+                                               rows=rows, align="bottom_right")
+        check("O", O[0, h, rows], Or, BF16_O_TOL)
+        check("lse", L[0, h, rows], Lr, BF16_LSE_TOL)
+
+
 def test_single_head_f32_workload():
     """B=1, H=1, T=256, d=64, fp32, non-causal, seed 0."""
     w = inputs.SINGLE_HEAD_F32
