@@ -126,6 +126,7 @@ class Decode:
     seq_lo: int
     seq_hi: int
     seed: int = 0
+    kv_dtype: str = "bf16"       # "bf16", or "fp8": E4M3 codes with one fp32 scale per row
 
     @property
     def scale(self) -> float:
@@ -151,6 +152,11 @@ LLAMA3_8B_CHUNK = Prefill("Llama-3-8B GQA chunked prefill, last 4096 of 32768 po
 FLASH_DECODE = Decode("split-KV decode, B=16, Hq=32, Hkv=8, d=128, seqlen U[1024,32768]",
                       B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768)
 
+FLASH_DECODE_FP8 = Decode("split-KV decode over an fp8 (E4M3, per-row scale) cache, B=16, Hq=32, "
+                          "Hkv=8, d=128, seqlen U[1024,32768]",
+                          B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768,
+                          kv_dtype="fp8")
+
 WORKLOADS = {
     "single_head_f32": SINGLE_HEAD_F32,
     "gpt2_small_mha": GPT2_SMALL_MHA,
@@ -158,6 +164,7 @@ WORKLOADS = {
     "llama3_8b_long": LLAMA3_8B_LONG,
     "llama3_8b_chunk": LLAMA3_8B_CHUNK,
     "flash_decode": FLASH_DECODE,
+    "flash_decode_fp8": FLASH_DECODE_FP8,
 }
 
 
@@ -213,3 +220,44 @@ def decode_inputs(w: Decode, *, seed: Optional[int] = None, poison_tail: bool = 
             kc[b, :, n:, :] = BF16_NAN
             vc[b, :, n:, :] = BF16_NAN
     return q, kc, vc, seqlens
+
+
+E4M3_MAX = 448.0   # largest finite E4M3 value
+
+
+def quantize_rows_e4m3(x: np.ndarray):
+    """Per-row block scaling of fp32 rows (last axis) to 8-bit E4M3 codes, as a
+    cache writer would store them: scale = max|row| / 448 (1 for an all-zero
+    row), codes = round-to-nearest-even of row / scale, done by torch's
+    float8_e4m3fn conversion.  Returns (codes uint8, scales float32)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[..., None]).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def decode_inputs_fp8(w: Decode, *, seed: Optional[int] = None, poison_tail: bool = False):
+    """Return (q, kcodes, vcodes, kscale, vscale, seqlens) for an fp8-cache decode.
+
+    seqlens, q, k and v are drawn exactly as ``decode_inputs`` draws them
+    (q rounded to bf16); the fp32 k and v rows are then stored as E4M3 codes
+    with one fp32 scale per (sequence, kv head, position).  With
+    ``poison_tail`` every slot at or beyond seqlens[b] holds the NaN code 0x7F.
+    """
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    seqlens = rng.integers(w.seq_lo, w.seq_hi, w.B, endpoint=True).astype(np.int32)
+    q = _draw(rng, (w.B, w.Hq, w.d), "bf16")
+    k = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "f32")
+    v = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "f32")
+    kc, ks = quantize_rows_e4m3(k)
+    del k
+    vc, vs = quantize_rows_e4m3(v)
+    del v
+    if poison_tail:
+        for b, n in enumerate(seqlens):
+            kc[b, :, n:, :] = 0x7F
+            vc[b, :, n:, :] = 0x7F
+    return q, kc, vc, ks, vs, seqlens

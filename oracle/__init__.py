@@ -23,6 +23,8 @@ from .attention import (  # noqa: F401
     online_fold_attention,
     attention_backward,
     decode_attention,
+    decode_attention_fp8,
+    e4m3_to_f64,
     decode_split_merge,
     online_normalizer,
     online_weighted_sum,

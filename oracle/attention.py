@@ -342,6 +342,50 @@ def decode_attention(q, kcache, vcache, seqlens) -> Tuple[np.ndarray, np.ndarray
     return O, L
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Values of 8-bit floating-point codes in the E4M3 format with no
+    infinities (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent field 0 encodes subnormals m/8 * 2^-6; the all-ones exponent and
+    mantissa, 0x7F and 0xFF, is NaN; largest finite value 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def decode_attention_fp8(q, kcodes, vcodes, kscale, vscale, seqlens) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over an 8-bit cache: dequantize, then the decode definition.
+
+    The cache holds E4M3 codes kcodes, vcodes:[B,Hkv,Tk_max,d] and one fp32
+    scale per cached row kscale, vscale:[B,Hkv,Tk_max]; row j of kv head h
+    stands for K[b,h,j,:] = kscale[b,h,j] * e4m3(kcodes[b,h,j,:]) (and V
+    alike) -- a per-row block scale, the plain form of a block-scaled low-bit
+    cache ([NOTE] section on fused dequantisation: the cache is stored
+    compressed and expanded inside the attention kernel's tile load).  The
+    attention over the expanded rows is exactly ``decode_attention``; rows at
+    or past seqlens[b] are never read.
+    """
+    B, Hq, d = q.shape
+    Hkv = kcodes.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, vcodes.shape[3]))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in range(B):
+        n = int(seqlens[b])
+        for kh in range(Hkv):
+            K = e4m3_to_f64(kcodes[b, kh, :n]) * np.asarray(kscale[b, kh, :n], np.float64)[:, None]
+            V = e4m3_to_f64(vcodes[b, kh, :n]) * np.asarray(vscale[b, kh, :n], np.float64)[:, None]
+            for h in range(kh * g, (kh + 1) * g):
+                Qr = as_f64(q[b, h])[None, :]
+                o, lse = _rows_three_pass(Qr, K, V, scale, np.ones((1, n), bool))
+                O[b, h], L[b, h] = o[0], lse[0]
+    return O, L
+
+
 def decode_split_merge(q, kcache, vcache, seqlens, num_splits: int,
                        tile: int = 64) -> Tuple[np.ndarray, np.ndarray]:
     """Flash-decoding in fp64: split each sequence's keys, merge the partials.

@@ -657,3 +657,70 @@ def test_causal_offset_values():
     assert oracle.causal_offset(9, 5, "bottom_right") == -4
     with pytest.raises(ValueError):
         oracle.causal_offset(1, 1, "middle")
+
+
+# ---------------------------------------------------------------------------
+# Decode over an 8-bit (E4M3, per-row scale) cache
+# ---------------------------------------------------------------------------
+
+def test_e4m3_decoder_matches_torch_all_codes():
+    """Library routine: torch's float8_e4m3fn widening of all 256 codes."""
+    torch = pytest.importorskip("torch")
+    c = np.arange(256, dtype=np.uint8)
+    a = oracle.e4m3_to_f64(c)
+    b = torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+
+
+def test_e4m3_format_values():
+    """Values fixed by the format: zero, one, the extremes, subnormals, NaN."""
+    v = oracle.e4m3_to_f64(np.array([0x00, 0x80, 0x38, 0xB8, 0x7E, 0xFE, 0x01, 0x07, 0x08, 0x40,
+                                     0x7F, 0xFF], np.uint8))
+    assert v[0] == 0 and v[1] == 0 and math.copysign(1, v[1]) == -1
+    assert v[2] == 1.0 and v[3] == -1.0
+    assert v[4] == 448.0 and v[5] == -448.0
+    assert v[6] == 2.0 ** -9 and v[7] == 7 * 2.0 ** -9 and v[8] == 2.0 ** -6
+    assert v[9] == 2.0
+    assert np.isnan(v[10]) and np.isnan(v[11])
+
+
+def _small_fp8_decode(poison=False):
+    w = inputs.Decode("t", B=3, Hq=8, Hkv=2, Tk_max=70, d=16, seq_lo=0, seq_hi=70, seed=5,
+                      kv_dtype="fp8")
+    return inputs.decode_inputs_fp8(w, poison_tail=poison)
+
+
+def test_fp8_decode_is_decode_of_the_dequantized_cache():
+    """Dequantised with torch's E4M3 widening times the row scales, the cache
+    gives the same result through the plain decode definition."""
+    torch = pytest.importorskip("torch")
+    q, kc, vc, ks, vs, sl = _small_fp8_decode()
+    O, L = oracle.decode_attention_fp8(q, kc, vc, ks, vs, sl)
+    K = torch.from_numpy(kc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * ks[..., None]
+    V = torch.from_numpy(vc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * vs[..., None]
+    Or, Lr = oracle.decode_attention(q, K, V, sl)
+    assert np.array_equal(np.isinf(L), np.isinf(Lr))
+    assert np.max(np.abs(O - Or)) < 1e-14
+    fin = np.isfinite(Lr)
+    assert np.max(np.abs(L[fin] - Lr[fin])) < 1e-14
+
+
+def test_fp8_decode_ignores_cache_beyond_seqlen():
+    q, kc, vc, ks, vs, sl = _small_fp8_decode(poison=False)
+    O, L = oracle.decode_attention_fp8(q, kc, vc, ks, vs, sl)
+    q2, kc2, vc2, ks2, vs2, sl2 = _small_fp8_decode(poison=True)
+    O2, L2 = oracle.decode_attention_fp8(q2, kc2, vc2, ks2, vs2, sl2)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_fp8_row_quantisation_uses_the_full_range():
+    """Input side: every stored row's largest code is +-448 (amax scaling),
+    and scale * code reproduces the drawn value to E4M3 precision."""
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((5, 7, 32)).astype(np.float32)
+    codes, sc = inputs.quantize_rows_e4m3(x)
+    vals = oracle.e4m3_to_f64(codes)
+    assert np.all(np.max(np.abs(vals), axis=-1) == 448.0)
+    rel = np.abs(vals * sc[..., None] - x) / np.max(np.abs(x), axis=-1, keepdims=True)
+    assert np.max(rel) <= 16 / 448   # half the E4M3 spacing (32) of the top binade, relative to amax
