@@ -107,18 +107,19 @@ constexpr int kMaxDecodeWorkgroups = 1 << 20;
 // Workgroups for a decode call: the caller's count, or (0) as many as the
 // device keeps resident at once, so that every workgroup starts at launch
 // and all of them finish together.  Cached per (device, d, heads per
-// workgroup).  Returns a negative status if the device cannot be queried.
-int decode_workgroups(int d, int hpw, int num_splits) {
+// workgroup, cache type).  Returns a negative status if the device cannot be
+// queried.
+int decode_workgroups(int d, int hpw, bool fp8, int num_splits) {
   if (num_splits > 0) return num_splits < kMaxDecodeWorkgroups ? num_splits : kMaxDecodeWorkgroups;
   static std::mutex mu;
   static std::map<std::pair<int, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -FA_ERR_DEVICE;
-  const std::pair<int, int> key(dev, d * 16 + hpw);
+  const std::pair<int, int> key(dev, (d * 16 + hpw) * 2 + (fp8 ? 1 : 0));
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  const int w = fa::decode_resident_workgroups(d, hpw);
+  const int w = fa::decode_resident_workgroups(d, hpw, fp8);
   if (w <= 0) return -FA_ERR_DEVICE;
   cache[key] = w;
   return w;
@@ -215,27 +216,31 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   return map_err(fa::launch_bwd(p, d, causal != 0, hs));
 }
 
-int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
+namespace {
+
+int decode_workgroups_checked(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, bool fp8) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0 || Hq % Hkv != 0)
     return -FA_ERR_SHAPE;
   if (d != 64 && d != 128) return -FA_ERR_UNSUPPORTED;
-  return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), num_splits);
+  return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), fp8, num_splits);
 }
 
-int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens, void* o,
-              int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, void* stream) {
+int decode_impl(const void* q, const void* kcache, const void* vcache, const float* kscale,
+                const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
+                int Tk_max, int d, int num_splits, bool fp8, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Hq == 0) return FA_OK;
   if (q == nullptr || o == nullptr || seqlens == nullptr) return FA_ERR_NULL;
   if (Tk_max > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_NULL;
+  if (fp8 && Tk_max > 0 && (kscale == nullptr || vscale == nullptr)) return FA_ERR_NULL;
   // One merge wavefront per (sequence, query head).
   if ((int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
 
   const int g = Hq / Hkv;
   const int hpw = fa::decode_heads_per_workgroup(g);
-  const int W = decode_workgroups(d, hpw, num_splits);
+  const int W = decode_workgroups(d, hpw, fp8, num_splits);
   if (W < 0) return -W;
   const size_t slots = fa::decode_slots(W, B, Hkv, g, hpw);
   const size_t cum_bytes = (((size_t)B + 1) * sizeof(long long) + 255) / 256 * 256;
@@ -251,6 +256,8 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   p.q = q;
   p.kcache = kcache;
   p.vcache = vcache;
+  p.kscale = fp8 ? kscale : nullptr;
+  p.vscale = fp8 ? vscale : nullptr;
   p.seqlens = seqlens;
   p.o = o;
   p.cum = (long long*)ws;
@@ -265,7 +272,30 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
   p.hpw = hpw;
   p.W = W;
   p.c = (float)(1.4426950408889634 / sqrt((double)d));
-  return map_err(fa::launch_decode(p, d, hs));
+  return map_err(fa::launch_decode(p, d, fp8, hs));
+}
+
+}  // namespace
+
+int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
+  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, false);
+}
+
+int fa_decode_fp8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
+  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, true);
+}
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens, void* o,
+              int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, void* stream) {
+  return decode_impl(q, kcache, vcache, nullptr, nullptr, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                     num_splits, false, stream);
+}
+
+int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* kscale,
+                  const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
+                  int Tk_max, int d, int num_splits, void* stream) {
+  return decode_impl(q, kcache, vcache, kscale, vscale, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                     num_splits, true, stream);
 }
 
 int fa_read_probe(const void* src, size_t bytes, unsigned* sink, void* stream) {

@@ -15,7 +15,7 @@
 //           reproducible).
 //
 // This work is bound by HBM bandwidth (about 4 FLOP per cache byte with a
-// group of 4), so it runs on the vector ALUs; the design goal is to stream
+// group of 4; 8 with an 8-bit cache), so it runs on the vector ALUs; the design goal is to stream
 // every cache byte exactly once with coalesced 16-byte loads and enough
 // loads in flight, while spending as few vector instructions per key as
 // possible so that the arithmetic hides under the memory time.
@@ -44,6 +44,9 @@
 //  * At the end the rows of a wavefront are merged with the rescale rule
 //    (lane shuffles), then the 4 wavefronts through LDS, and the piece's
 //    (m, l, o) is written to the workspace.
+// An 8-bit cache (E4M3 codes, one fp32 scale per row: [NOTE]'s fused
+// dequantisation, the cache expanded inside the tile load) runs the same
+// loop: the codes are widened to bf16 in registers right after the load.
 // Merge kernel, one wavefront per (sequence, query head): fixed-order pass
 // over the pieces, O = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.
 #include "fa_device.h"
@@ -109,10 +112,31 @@ struct DecodeShape {
   static constexpr int NV = EPL / 8;
 };
 
+// Widen 4 E4M3 codes (one word) to two words of bf16 pairs, in order; the
+// conversion is exact (every E4M3 value is a bf16 value).
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  uint32_t lo, hi;
+  __builtin_memcpy(&lo, &a, 4);
+  __builtin_memcpy(&hi, &b, 4);
+  return u32x2{lo, hi};
+}
+// Widen 8 E4M3 codes (two words) to one 16-byte vector of bf16 pairs.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const u32x2 a = e4m3x4_to_bf16(w0);
+  const u32x2 b = e4m3x4_to_bf16(w1);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
 // Attention of the HPW query heads hq0.. over keys [lo, hi) of kv head
 // (b, kvh); the partial (m, l, o) goes to `slot`.  Every thread of the
-// workgroup calls this with the same arguments.
-template <int D, int HPW, int KU>
+// workgroup calls this with the same arguments.  FP8: the cache holds E4M3
+// codes with one fp32 scale per row; a lane loads its EPL codes with one
+// load, widens them to bf16 in registers and the rest of the loop is the
+// bf16 one, with the K row scale applied to the row's score and the V row
+// scale to its probability (after the row sum l is formed).
+template <int D, int HPW, int KU, bool FP8>
 __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, int kvh, int hq0,
                                                   int lo, int hi, size_t slot, float (*red_m)[HPW],
                                                   float (*red_l)[HPW], float (*red_o)[HPW][D]) {
@@ -128,8 +152,9 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
   const int dl = lane % LPR;
   const float c = p.c;
 
-  // Element offset of vector j of this lane inside a row.
-  auto eoff = [&](int j) { return j * (D / NV) + dl * 8; };
+  // Element offset of vector j of this lane inside a row (FP8: the lane's
+  // EPL elements are contiguous so that one load fetches them).
+  auto eoff = [&](int j) { return FP8 ? dl * EPL + 8 * j : j * (D / NV) + dl * 8; };
 
   u32x4 qv[HPW][NV];
 #pragma unroll
@@ -141,6 +166,9 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
   const size_t head_off = ((size_t)b * p.Hkv + kvh) * p.Tk_max * D;
   const bf16* Kg = (const bf16*)p.kcache + head_off;
   const bf16* Vg = (const bf16*)p.vcache + head_off;
+  const uint8_t* Kg8 = (const uint8_t*)p.kcache + head_off;
+  const uint8_t* Vg8 = (const uint8_t*)p.vcache + head_off;
+  const size_t srow = ((size_t)b * p.Hkv + kvh) * p.Tk_max;   // row-scale index of key 0
 
   float m[HPW], l[HPW], o[HPW][EPL];
 #pragma unroll
@@ -156,19 +184,47 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
     // Key of load step u of this lane: k0 + u * RPW.
     const int k0 = base + wave * RPW * KU + row;
     u32x4 kr[KU][NV], vr[KU][NV];
+    float ks[KU], vs[KU];   // FP8: row scales (0 past the range)
+    if constexpr (FP8) {
+      // EPL codes per lane: one 16- or 8-byte load per row and tensor.
+      typedef uint32_t raw_t __attribute__((ext_vector_type(EPL / 4)));
+      raw_t kb[KU], vb[KU];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int key = k0 + u * RPW;
+      for (int u = 0; u < KU; ++u) {
+        const int key = k0 + u * RPW;
+        const bool in = key < hi;
+        kb[u] = in ? *(const raw_t*)(Kg8 + (size_t)key * D + dl * EPL) : raw_t{};
+        ks[u] = in ? p.kscale[srow + key] : 0.f;
+      }
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        kr[u][j] = key < hi ? *(const u32x4*)(Kg + (size_t)key * D + eoff(j)) : zero;
-    }
+      for (int u = 0; u < KU; ++u) {
+        const int key = k0 + u * RPW;
+        const bool in = key < hi;
+        vb[u] = in ? *(const raw_t*)(Vg8 + (size_t)key * D + dl * EPL) : raw_t{};
+        vs[u] = in ? p.vscale[srow + key] : 0.f;
+      }
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int key = k0 + u * RPW;
+      for (int u = 0; u < KU; ++u)
 #pragma unroll
-      for (int j = 0; j < NV; ++j)
-        vr[u][j] = key < hi ? *(const u32x4*)(Vg + (size_t)key * D + eoff(j)) : zero;
+        for (int j = 0; j < NV; ++j) {
+          kr[u][j] = e4m3x8_to_bf16(kb[u][2 * j], kb[u][2 * j + 1]);
+          vr[u][j] = e4m3x8_to_bf16(vb[u][2 * j], vb[u][2 * j + 1]);
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int key = k0 + u * RPW;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          kr[u][j] = key < hi ? *(const u32x4*)(Kg + (size_t)key * D + eoff(j)) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int key = k0 + u * RPW;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          vr[u][j] = key < hi ? *(const u32x4*)(Vg + (size_t)key * D + eoff(j)) : zero;
+      }
     }
 
     // Scores, reduced over the LPR lanes of each row.
@@ -185,6 +241,7 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
             acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][j][w]), as_bf16x2(qv[h][j][w]),
                                                   acc, false);
         sc[u][h] = LPR == 8 ? group8_sum(acc) : group16_sum(acc);
+        if constexpr (FP8) sc[u][h] *= ks[u];
       }
     if (base + STEP > hi) {   // last iteration: keys past the range get -inf
 #pragma unroll
@@ -218,6 +275,10 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
       for (int u = 0; u < KU; ++u) {
         pe[u] = exp2_fast(fmaf(sc[u][h], c, -mc));
         l[h] += pe[u];
+      }
+      if constexpr (FP8) {
+#pragma unroll
+        for (int u = 0; u < KU; ++u) pe[u] *= vs[u];
       }
 #pragma unroll
       for (int t = 0; t < KU / 2; ++t) pp[t][h] = bf16_pair_bits(pe[2 * t], pe[2 * t + 1]);
@@ -296,7 +357,7 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
 }
 
 // Workgroup w of W: balanced share of the key space of all segments.
-template <int D, int HPW, int KU>
+template <int D, int HPW, int KU, bool FP8>
 __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams p) {
   __shared__ float red_m[4][HPW];
   __shared__ float red_l[4][HPW];
@@ -374,8 +435,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams 
     const int cnt = (int)min((long long)(n - key), pend - pos);
     const int kvh = j / groups;
     const int hq0 = kvh * p.g + (j % groups) * HPW;
-    decode_range_keys<D, HPW, KU>(p, b, kvh, hq0, key, key + cnt, (size_t)w + (size_t)b * G + j,
-                                  red_m, red_l, red_o);
+    decode_range_keys<D, HPW, KU, FP8>(p, b, kvh, hq0, key, key + cnt,
+                                       (size_t)w + (size_t)b * G + j, red_m, red_l, red_o);
     pos += cnt;
     if (pos >= pend) break;
     key = 0;
@@ -478,29 +539,29 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) 
   }
 }
 
-template <int D, int HPW>
+template <int D, int HPW, bool FP8>
 const void* decode_kernel_ptr() {
-  return (const void*)decode_kernel<D, HPW, kDecKU>;
+  return (const void*)decode_kernel<D, HPW, kDecKU, FP8>;
 }
 
-template <int D>
+template <int D, bool FP8>
 const void* decode_kernel_for(int hpw) {
   switch (hpw) {
-    case 8: return decode_kernel_ptr<D, 8>();
-    case 4: return decode_kernel_ptr<D, 4>();
-    case 2: return decode_kernel_ptr<D, 2>();
-    default: return decode_kernel_ptr<D, 1>();
+    case 8: return decode_kernel_ptr<D, 8, FP8>();
+    case 4: return decode_kernel_ptr<D, 4, FP8>();
+    case 2: return decode_kernel_ptr<D, 2, FP8>();
+    default: return decode_kernel_ptr<D, 1, FP8>();
   }
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.W);
   switch (p.hpw) {
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, kDecKU>), grid, dim3(kDecThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, kDecKU>), grid, dim3(kDecThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, kDecKU>), grid, dim3(kDecThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, 1, kDecKU>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, 1, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -510,15 +571,17 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream) {
-  return d == 64 ? launch_decode_d<64>(p, stream) : launch_decode_d<128>(p, stream);
+hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
+  if (fp8) return d == 64 ? launch_decode_d<64, true>(p, stream) : launch_decode_d<128, true>(p, stream);
+  return d == 64 ? launch_decode_d<64, false>(p, stream) : launch_decode_d<128, false>(p, stream);
 }
 
-int decode_resident_workgroups(int d, int hpw) {
+int decode_resident_workgroups(int d, int hpw, bool fp8) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* k = d == 64 ? decode_kernel_for<64>(hpw) : decode_kernel_for<128>(hpw);
+  const void* k = fp8 ? (d == 64 ? decode_kernel_for<64, true>(hpw) : decode_kernel_for<128, true>(hpw))
+                      : (d == 64 ? decode_kernel_for<64, false>(hpw) : decode_kernel_for<128, false>(hpw));
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kDecThreads, 0) != hipSuccess) return 0;
   return cus * per_cu;
 }

@@ -29,8 +29,10 @@ struct FwdParams {
 // w + segment.  The merge kernel combines the slots of each segment.
 struct DecodeParams {
   const void* q;
-  const void* kcache;
+  const void* kcache;   // bf16, or E4M3 codes (one byte per element)
   const void* vcache;
+  const float* kscale;  // E4M3 cache: one scale per row, [B, Hkv, Tk_max]; else null
+  const float* vscale;
   const int* seqlens;
   void* o;
   long long* cum;  // [B + 1] exclusive prefix sums of the clamped sequence lengths
@@ -77,10 +79,10 @@ int compute_units();
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int d, hipStream_t stream);
-// Workgroups that the decode kernel for (d, hpw) keeps resident on the
-// current device at once; 0 if the device cannot be queried.
-int decode_resident_workgroups(int d, int hpw);
+hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
+// Workgroups that the decode kernel for (d, hpw, cache type) keeps resident
+// on the current device at once; 0 if the device cannot be queried.
+int decode_resident_workgroups(int d, int hpw, bool fp8);
 // Streams `bytes` (a multiple of 16) from src once, XOR-folding them into
 // *sink (which the caller zeroes).
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t stream);

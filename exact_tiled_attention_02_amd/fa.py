@@ -1,6 +1,7 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
 The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
+``fa_decode_fp8``, ``fa_decode_fp8_workgroups``,
 ``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
 with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
@@ -58,6 +59,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode.restype = I
         lib.fa_decode_workgroups.argtypes = [I, I, I, I, I, I]
         lib.fa_decode_workgroups.restype = I
+        lib.fa_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.fa_decode_fp8.restype = I
+        lib.fa_decode_fp8_workgroups.argtypes = [I, I, I, I, I, I]
+        lib.fa_decode_fp8_workgroups.restype = I
         lib.fa_strerror.argtypes = [I]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
@@ -135,6 +140,20 @@ def fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
     n = load().fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, int(num_splits))
     if n < 0:
         raise FAError(-n, "fa_decode_workgroups")
+    return n
+
+
+def fa_decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                  num_splits, stream=None) -> None:
+    _check(load().fa_decode_fp8(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kscale), _ptr(vscale),
+                                _ptr(seqlens), _ptr(o), B, Hq, Hkv, Tk_max, d, int(num_splits),
+                                _stream(stream)), "fa_decode_fp8")
+
+
+def fa_decode_fp8_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
+    n = load().fa_decode_fp8_workgroups(B, Hq, Hkv, Tk_max, d, int(num_splits))
+    if n < 0:
+        raise FAError(-n, "fa_decode_fp8_workgroups")
     return n
 
 
@@ -254,3 +273,28 @@ def attention_backward(q, k, v, o, lse, dout, *, causal: bool, scale: float | No
         stream = torch.cuda.current_stream(q.device)
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream)
     return dq, dk, dv
+
+
+def decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, *, num_splits: int = 0, out=None,
+               stream=None):
+    """Single-query attention over an E4M3 KV cache: q [B,Hq,d] bf16, caches
+    [B,Hkv,Tmax,d] uint8 codes, scales [B,Hkv,Tmax] fp32, seqlens [B] int32."""
+    import torch
+    _require(q.dim() == 3 and kcache.dim() == 4 and vcache.shape == kcache.shape, "bad shapes")
+    _require(q.dtype == torch.bfloat16 and kcache.dtype == vcache.dtype == torch.uint8,
+             "q must be bf16 and the caches uint8 E4M3 codes")
+    _require(kscale.dtype == vscale.dtype == torch.float32 and
+             tuple(kscale.shape) == tuple(vscale.shape) == tuple(kcache.shape[:3]),
+             "scales must be fp32 [B,Hkv,Tmax]")
+    _require(seqlens.dtype == torch.int32 and seqlens.is_cuda, "seqlens must be int32 on the GPU")
+    _require(all(t.is_contiguous() for t in (q, kcache, vcache, kscale, vscale)),
+             "tensors must be contiguous")
+    B, Hq, d = q.shape
+    _, Hkv, Tmax, _ = kcache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fa_decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, out, B, Hq, Hkv, Tmax, d, num_splits,
+                  stream)
+    return out

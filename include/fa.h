@@ -195,6 +195,34 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
 int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
 
 /*
+ * fa_decode_fp8 -- fa_decode over an 8-bit KV cache, dequantised inside the
+ * kernel as each row is loaded ([NOTE] section "Prefill i dekodowanie to
+ * różne problemy": decode streams the cache, so the bytes per cached key set
+ * its speed, and a compressed cache is expanded in the attention kernel's
+ * tile load rather than by a separate pass).
+ *
+ *   kcache, vcache : [B, Hkv, Tk_max, d] uint8 codes in the E4M3 format with
+ *                    no infinities (OCP FP8 E4M3: bias 7, 3 mantissa bits,
+ *                    largest finite 448, 0x7F/0xFF NaN)
+ *   kscale, vscale : [B, Hkv, Tk_max] fp32, one scale per cached row
+ * Row j of kv head h of sequence b stands for
+ *     K[b,h,j,:] = kscale[b,h,j] * e4m3(kcache[b,h,j,:])   (V alike),
+ * and the result is exact attention of the query over those rows, with the
+ * same contract as fa_decode (q and o bf16, seqlens on the device, scale
+ * 1/sqrt(d), num_splits, workspace, determinism, errors; FA_ERR_NULL also for
+ * a NULL scale array when Tk_max > 0).  Arithmetic: codes widen exactly to
+ * bf16; q.k as packed bf16 dot products with fp32 sums, times the K row
+ * scale; the probability times the V row scale is rounded to bf16 for the
+ * p.v product; the row sums use the unscaled fp32 probabilities.
+ */
+int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* kscale,
+                  const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
+                  int Tk_max, int d, int num_splits, void* stream);
+
+/* fa_decode_workgroups for fa_decode_fp8. */
+int fa_decode_fp8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
+
+/*
  * fa_read_probe -- measurement utility, not part of the attention path:
  * reads `bytes` bytes of device memory at `src` exactly once with 16-byte
  * loads (one 1 MiB chunk per workgroup, several loads in flight per lane)

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_decode", "fa_strerror",
-              "fa_release_workspace", "fa_decode_workgroups", "fa_read_probe"):
+              "fa_release_workspace", "fa_decode_workgroups", "fa_read_probe", "fa_decode_fp8",
+              "fa_decode_fp8_workgroups"):
         assert n in names
 
 
@@ -107,6 +108,22 @@ def test_bwd_validation(lib, args, status):
 ])
 def test_decode_validation(lib, args, status):
     assert lib.fa_decode(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, kc, vc, ks, vs, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits)
+    ((FAKE,) * 7 + (2, 8, 2, 64, 32, 4), 3),
+    ((FAKE,) * 7 + (2, 8, 3, 64, 128, 4), 2),
+    ((FAKE,) * 7 + (2, 8, 2, 64, 128, -1), 2),
+    ((FAKE, FAKE, FAKE, P, FAKE, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # kscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, P, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # vscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, P, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # seqlens NULL
+    ((FAKE, P, FAKE, FAKE, FAKE, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # kcache NULL
+    ((P,) * 7 + (0, 8, 2, 64, 128, 4), 0),                                  # empty batch
+    ((FAKE,) * 7 + (1 << 28, 8, 2, 64, 128, 4), 2),
+])
+def test_decode_fp8_validation(lib, args, status):
+    assert lib.fa_decode_fp8(*args, None) == status
 
 
 def test_decode_workgroup_planning(lib):
