@@ -164,6 +164,20 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return map_err(fa::launch_fwd_f32(p, d, causal != 0, (hipStream_t)stream));
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* qscale,
+               const float* kscale, const float* vscale, void* o, float* lse, int B, int Hq,
+               int Hkv, int Tq, int Tk, int d, int causal, float scale, void* stream) {
+  bool empty = false;
+  const int st = check_fwd(q, k, v, o, B, Hq, Hkv, Tq, Tk, d, causal, scale, &empty);
+  if (st != FA_OK || empty) return st;
+  if (qscale == nullptr || kscale == nullptr || vscale == nullptr) return FA_ERR_NULL;
+  fa::FwdParams p = make_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale);
+  p.qscale = qscale;
+  p.kscale = kscale;
+  p.vscale = vscale;
+  return map_err(fa::launch_fwd_fp8(p, d, causal != 0, (hipStream_t)stream));
+}
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk,
            int d, int causal, float scale, void* stream) {

@@ -1,0 +1,397 @@
+// FlashAttention forward (prefill) over 8-bit inputs for gfx950.
+//
+// Sources (web pages; sections named as headed there):
+//   [LESSON] "FlashAttention: внимание без матрицы n×n" (ai.flicky.cc),
+//            section "Прямой проход FlashAttention" (the tiled loop) and
+//            section "FlashAttention-2, -3 и дальше" (FA-3: FP8 with block
+//            scaling).
+//   [FA3QA]  "Как работает FlashAttention-3 математически?" (aivaro.ru),
+//            section 6 (FP8 support: E4M3 inputs, higher-precision
+//            accumulation).
+//   [BOOK5]  "Глава 5. Операторы и среда выполнения" (bojieli.github.io),
+//            section 5.4.3, Example 5-7 (a row scale is fixed by the whole
+//            row's maximum before any element is quantised).
+//
+// Inputs are E4M3 codes with block scales: every query row has its own
+// scale (q_i = qs_i * e4m3(q8_i)), and each (batch, kv head) has one scale
+// for K and one for V.  The result is exact attention of those dequantised
+// inputs up to the rounding stated here: q.k products of 8-bit values are
+// exact and summed in fp32 on the matrix core (32x32x64 8-bit MFMA); the
+// online softmax runs in fp32 as in the bf16 kernel; the probabilities are
+// rounded to E4M3 for the P.V product (P times 448, so that the largest
+// probability of a row, exactly 1, maps to the largest code), which is the
+// one rounding step that the 16-bit kernel does in bf16.
+//
+// Mapping onto CDNA4 (the bf16 kernel's design with 8-bit operands):
+//  * 512 threads = 8 wavefronts of 32 query rows; HG query heads of a GQA
+//    group share each K/V tile; 4 LDS stages filled by buffer-resource
+//    copies three tiles ahead; causal pairing of light and heavy half-tiles
+//    on small grids.
+//  * S^T = K Q^T with one 32x32x64 MFMA per 64 head dimensions: lane l
+//    supplies 32 bytes of its key row (A) or query row (B) for head
+//    dimensions 64c + 32*(l/32) .. +32; the instruction sums over both lane
+//    halves' bytes, so any byte order used alike on both sides is correct.
+//  * O^T += V^T P^T with one MFMA per 64 keys and 32 head dimensions: the
+//    probabilities come straight from the score registers (byte p of lane l
+//    is key kappa(p) = 16*(p/8) + 8*((p%8)/4) + 4*(l/32) + p%4 of the tile),
+//    and V^T is gathered with the gfx950 transposing 8-bit LDS read in the
+//    same key order.
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_lds.h"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kF8Threads = 512;
+constexpr int kF8Stages = 4;
+constexpr int kF8BN = 64;                  // keys per tile
+constexpr float kLog2E4M3Max = 8.807354922057604f;   // log2(448)
+
+// Byte tiles (rows x D codes, row-major): 16-byte chunk c of row r sits at
+// position c ^ f8swz(r).  The function depends only on row bits that
+// separate rows sharing an LDS bank line (1..3 at 128-byte rows, 2..3 at
+// 64-byte rows): 16 consecutive rows read at one chunk hit distinct banks,
+// and so do the 8 rows {0..3, 8..11} (+4) that one transposing read
+// gathers.  Rows r and r + 16i get the same value.
+template <int D>
+__device__ __forceinline__ int f8swz(int r) {
+  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+
+// 32x32x64 MFMA on E4M3 operands with unit block scales.
+__device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Four fp32 values (already within +-448) to E4M3 codes in one word, in order.
+__device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__device__ __forceinline__ float max_halves8(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves8(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, bool CAUSAL, int HG>
+__global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams p) {
+  constexpr int NW = kF8Threads / 64;
+  constexpr int WPH = NW / HG;           // wavefronts per query head
+  constexpr int BMPOS = 32 * WPH;        // query positions per workgroup
+  constexpr int TILE = kF8BN * D;        // bytes of one K or V tile
+  constexpr int NC8 = D / 64;            // 64-deep steps of the Q.K product
+  constexpr int ND = D / 32;             // 32-wide blocks of the output
+  constexpr int CPR = D / 16;            // 16-byte chunks per row
+  constexpr int CW = TILE / 1024;        // wavefronts that copy (one 16-byte chunk per lane)
+  static_assert(CW >= 1 && CW <= NW, "tile size and workgroup do not match");
+  static_assert((2 * kF8Stages - 1) * TILE + 48 * D < 65536, "operand offsets must fit the immediate");
+  __shared__ __attribute__((aligned(16))) char lds[2 * kF8Stages * TILE];   // K0..K3 | V0..V3
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  int x = blockIdx.x;
+  const int grp = x % p.groups;
+  x /= p.groups;
+  const int kvh = x % p.Hkv;
+  const int b = x / p.Hkv;
+  const int hq = kvh * p.g + grp * HG + wave / WPH;
+  int q0w, q_end;
+  bool active = true;
+  if (CAUSAL && p.pair) {   // same pairing as the bf16 kernel
+    constexpr int HALF = BMPOS / 2;
+    const int nh = (p.Tq + HALF - 1) / HALF;
+    const int i = blockIdx.y;
+    const int hh = wave % WPH;
+    const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
+    const int ht = heavy ? nh - 1 - i : i;
+    active = !(heavy && ht == i);
+    q0w = ht * HALF + (hh % (WPH / 2)) * 32;
+    q_end = min(p.Tq, (nh - i) * HALF);
+  } else {
+    const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+    q0w = qt * BMPOS + (wave % WPH) * 32;
+    q_end = min(p.Tq, (qt + 1) * BMPOS);
+  }
+  const int my_q = q0w + col;
+
+  const size_t qplane = (size_t)b * p.Hq + hq;
+  const size_t kvplane = (size_t)b * p.Hkv + kvh;
+  const uint8_t* Qg = (const uint8_t*)p.q + qplane * p.Tq * D;
+  const uint8_t* Kg = (const uint8_t*)p.k + kvplane * p.Tk * D;
+  const uint8_t* Vg = (const uint8_t*)p.v + kvplane * p.Tk * D;
+
+  // This lane's query row as the B operand: 32 codes of head dimensions
+  // 64c + 32*half .. +32 (sign bits flipped for a negative scale).
+  i32x8 qf[NC8];
+  {
+    const uint32_t sgn = p.negate_q ? 0x80808080u : 0u;
+#pragma unroll
+    for (int c = 0; c < NC8; ++c) {
+      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+      if (my_q < p.Tq) {
+        const uint8_t* src = Qg + (size_t)my_q * D + 64 * c + 32 * half;
+        w0 = *(const u32x4*)src;
+        w1 = *(const u32x4*)(src + 16);
+      }
+      w0 ^= sgn;
+      w1 ^= sgn;
+      qf[c] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
+                    (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+    }
+  }
+  // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks.
+  const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
+  const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
+  const float vs = p.vscale[kvplane];
+
+  const int off = p.causal_off;
+  const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
+  const int ntiles = (kend + kF8BN - 1) / kF8BN;
+  const int my_tiles = !active ? 0
+                       : CAUSAL ? (q0w + 31 + off < 0 ? 0 : min(ntiles, (q0w + 31 + off) / kF8BN + 1))
+                                : ntiles;
+  const bool has_keys = !CAUSAL || my_q + off >= 0;
+
+  // Copies: wavefront w < CW fills LDS chunks [w*64, +64) of a tile; chunk
+  // L is row L / CPR at position L % CPR, holding chunk (L % CPR) ^ f8swz(row).
+  const int nbytes = p.Tk * D;
+  const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, nbytes, 0x00020000);
+  uint32_t csrc;
+  {
+    const int L = wave * 64 + lane;
+    const int row = L / CPR;
+    csrc = (uint32_t)(row * D + (((L % CPR) ^ f8swz<D>(row)) << 4));
+  }
+  auto issue_copies = [&](int t) __attribute__((always_inline)) {
+    if (wave >= CW) return;
+    const int st = t % kF8Stages;
+    const uint32_t soff = (uint32_t)t * TILE;
+    copy16_buf_to_lds(krsrc, lds + st * TILE + wave * 1024, csrc + soff, 0);
+    copy16_buf_to_lds(vrsrc, lds + (kF8Stages + st) * TILE + wave * 1024, csrc + soff, 0);
+  };
+  auto wait_copies = [&](int later) __attribute__((always_inline)) {
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<4>());
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2>());
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  };
+
+  // K operand bases (stage 0, key block 0): row `col`, chunks 4c + 2*half
+  // and 4c + 2*half + 1 (c < NC8).
+  uint32_t kread[2 * NC8];
+  {
+    const int sw = f8swz<D>(col);
+#pragma unroll
+    for (int i = 0; i < 2 * NC8; ++i) {
+      const int ch = 4 * (i >> 1) + 2 * half + (i & 1);
+      kread[i] = lds_addr(lds) + col * D + ((ch ^ sw) << 4);
+    }
+  }
+  // V^T operand bases for the transposing reads: input lane 2e + h of
+  // 16-lane group G addresses 8 codes, head dimensions 32*db + 16*(G%2) +
+  // 8h .. +8, of key row 8*(e/4) + 4*half + e%4 (plus 16j for read j, a
+  // compile-time offset that f8swz does not see).
+  uint32_t vread[ND];
+  {
+    const int t = lane & 15;
+    const int e = t >> 1, h = t & 1;
+    const int row = 8 * (e >> 2) + 4 * half + (e & 3);
+    const int sw = f8swz<D>(row);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int ch = 2 * db + ((lane >> 4) & 1);
+      vread[db] = lds_addr(lds + kF8Stages * TILE) + row * D + ((ch ^ sw) << 4) + 8 * h;
+    }
+  }
+
+  float m = kNegInf;   // running max of this row's raw 8-bit products
+  float l = 0.f;       // this half-wave's share of the running sum of 448 * P
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  for (int t = 0; t < min(ntiles, kF8Stages - 1); ++t) issue_copies(t);
+
+  auto tile = [&](int t, auto st_c) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    constexpr int KT = ST * TILE;
+    constexpr int VT = ST * TILE;   // vread already points at the V stages
+    const int t0 = t * kF8BN;
+    wait_copies(min(ntiles - 1 - t, kF8Stages - 2));
+    tile_barrier();
+    if (t + kF8Stages - 1 < ntiles) issue_copies(t + kF8Stages - 1);
+    if (t >= my_tiles) return;
+
+    // S^T for the two 32-key blocks.
+    u32x4 kr[2][2 * NC8];
+    static_for<0, 2 * NC8>([&](auto i_c) {
+      kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
+      kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
+    });
+    lgkm_wait<0>();
+#pragma unroll
+    for (int i = 0; i < 2 * NC8; ++i) {
+      tie(kr[0][i]);
+      tie(kr[1][i]);
+    }
+    f32x16 s[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NC8; ++c) {
+        const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[kb] = mma_f8(a, qf[c], s[kb]);
+      }
+
+    // V^T reads for the first half of the output blocks go out now; they do
+    // not depend on the probabilities.
+    constexpr int NDH = ND / 2;
+    u32x2 va[ND][4];
+    static_for<0, NDH>([&](auto db_c) {
+      static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
+    });
+
+    const bool need_mask = (t0 + kF8BN > p.Tk) || (CAUSAL && t0 + kF8BN - 1 > q0w + off);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
+          s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+    }
+    float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < 32; i += 2)
+      mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
+    mt = max_halves8(mt);
+    const float m_new = fmaxf(m, mt);
+    const float corr = has_keys ? exp2_fast((m - m_new) * cq) : 1.f;
+    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+#pragma unroll
+      for (int i = 0; i < ND; ++i) acc[i] *= corr;
+    }
+    l *= corr;
+    m = m_new;
+    // 448 * P = 2^(s*cq - m*cq + log2 448): the row's largest probability
+    // becomes the largest E4M3 value.
+    const float mc = has_keys ? m * cq - kLog2E4M3Max : 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
+        ls[r & 3] += s[kb][r];
+      }
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // B operand: byte 4w + i is key block w/4, register 4*(w%4) + i.
+    i32x8 pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r = 4 * (w & 3);
+      pb[w] = pack_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
+    }
+
+    lgkm_wait<0>();
+    static_for<NDH, ND>([&](auto db_c) {
+      static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
+    });
+#pragma unroll
+    for (int db = 0; db < NDH; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tie(va[db][j]);
+      const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
+                       (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
+      acc[db] = mma_f8(a, pb, acc[db]);
+    }
+    lgkm_wait<0>();
+#pragma unroll
+    for (int db = NDH; db < ND; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tie(va[db][j]);
+      const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
+                       (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
+      acc[db] = mma_f8(a, pb, acc[db]);
+    }
+  };
+  for (int t = 0; t < ntiles; t += kF8Stages) {
+    tile(t, IC<0>{});
+    if (t + 1 < ntiles) tile(t + 1, IC<1>{});
+    if (t + 2 < ntiles) tile(t + 2, IC<2>{});
+    if (t + 3 < ntiles) tile(t + 3, IC<3>{});
+  }
+
+  // O = acc * vs / l (the 448 of the probabilities cancels); lse in natural
+  // log: (m*cq + log2(l) - log2 448) * ln 2.
+  const float lt = sum_halves8(l);
+  const float inv = lt > 0.f ? vs / lt : 0.f;
+  if (active && my_q < p.Tq) {
+    bf16* Og = (bf16*)p.o + (qplane * p.Tq + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2 lo = to_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
+        const bf16x2 hi = to_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+        *(bf16x4*)(Og + 32 * db + 8 * j + 4 * half) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+      }
+    if (p.lse != nullptr && half == 0)
+      p.lse[qplane * p.Tq + my_q] =
+          lt > 0.f ? (m * cq + __builtin_amdgcn_logf(lt) - kLog2E4M3Max) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fp8_hg(const FwdParams& p0, hipStream_t stream) {
+  FwdParams p = p0;
+  const int hg = (p.g % 4 == 0) ? 4 : (p.g % 2 == 0) ? 2 : 1;
+  p.groups = p.g / hg;
+  const int bmpos = 32 * (kF8Threads / 64) / hg;
+  const int nx = p.B * p.Hkv * p.groups;
+  int ny = (p.Tq + bmpos - 1) / bmpos;
+  p.pair = 0;
+  if (CAUSAL && (long long)nx * ny < 4LL * compute_units()) {
+    const int half = bmpos / 2;
+    ny = ((p.Tq + half - 1) / half + 1) / 2;
+    p.pair = 1;
+  }
+  dim3 grid((unsigned)nx, (unsigned)ny);
+  if (hg == 4)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 4>), grid, dim3(kF8Threads), 0, stream, p);
+  else if (hg == 2)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 2>), grid, dim3(kF8Threads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 1>), grid, dim3(kF8Threads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream) {
+  if (d == 64) return causal ? launch_fp8_hg<64, true>(p, stream) : launch_fp8_hg<64, false>(p, stream);
+  return causal ? launch_fp8_hg<128, true>(p, stream) : launch_fp8_hg<128, false>(p, stream);
+}
+
+}  // namespace fa

@@ -18,6 +18,11 @@ struct FwdParams {
   int negate_q;    // scale < 0: queries are sign-flipped on load, c uses |scale|
   int pair;        // causal: workgroups pair mirrored light/heavy half-tiles
   int causal_off;  // causal: row i sees key j iff j <= i + causal_off (0 or Tk - Tq)
+  // 8-bit inputs only (E4M3 codes): q row scales [B,Hq,Tq], k and v scales
+  // per (batch, kv head) [B,Hkv].
+  const float* qscale;
+  const float* kscale;
+  const float* vscale;
 };
 
 // One decode call.  q,o: [B,Hq,d]; caches: [B,Hkv,Tk_max,d].
@@ -79,6 +84,7 @@ int compute_units();
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
 // Workgroups that the decode kernel for (d, hpw, cache type) keeps resident
 // on the current device at once; 0 if the device cannot be queried.

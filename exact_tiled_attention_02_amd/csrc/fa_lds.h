@@ -46,10 +46,31 @@ __device__ __forceinline__ u32x2 lds_read_tr(uint32_t addr) {
   return r;
 }
 
+// Transposing 8-bit LDS read (gfx950 ds_read_b64_tr_b8) at addr + OFF bytes:
+// within each group of 16 lanes, output lane 8*h + i receives byte i of the
+// 8 bytes addressed by input lanes 2e + h, e = 0..7 (in that order).  So if
+// input lane 2e + h addresses 8 consecutive bytes (columns c_h .. c_h + 7)
+// of row r_e of a row-major byte tile, output lane 8*h + i holds column
+// c_h + i of rows r_0 .. r_7.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
 // 16-byte LDS read at addr + OFF bytes.
 template <int OFF>
 __device__ __forceinline__ bf16x8 lds_read_b128(uint32_t addr) {
   bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+
+// 16-byte LDS read as four 32-bit words at addr + OFF bytes.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read_u32x4(uint32_t addr) {
+  u32x4 r;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }

@@ -1,6 +1,6 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
 ``fa_decode_fp8``, ``fa_decode_fp8_workgroups``,
 ``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
@@ -53,6 +53,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_fwd.restype = I
         lib.fa_fwd_f32.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         lib.fa_fwd_f32.restype = I
+        lib.fa_fwd_fp8.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
+        lib.fa_fwd_fp8.restype = I
         lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, P]
         lib.fa_bwd.restype = I
         lib.fa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
@@ -121,6 +123,13 @@ def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -
 def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale, stream=None) -> None:
     _check(load().fa_fwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk,
                              d, _causal(causal), float(scale), _stream(stream)), "fa_fwd_f32")
+
+
+def fa_fwd_fp8(q, k, v, qscale, kscale, vscale, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale,
+               stream=None) -> None:
+    _check(load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(qscale), _ptr(kscale), _ptr(vscale),
+                             _ptr(o), _ptr(lse), B, Hq, Hkv, Tq, Tk, d, _causal(causal),
+                             float(scale), _stream(stream)), "fa_fwd_fp8")
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, scale,

@@ -261,3 +261,34 @@ def decode_inputs_fp8(w: Decode, *, seed: Optional[int] = None, poison_tail: boo
             kc[b, :, n:, :] = 0x7F
             vc[b, :, n:, :] = 0x7F
     return q, kc, vc, ks, vs, seqlens
+
+
+def quantize_blocks_e4m3(x: np.ndarray, nblock_axes: int):
+    """Block scaling over the last `nblock_axes` axes: one scale per block,
+    scale = max|block| / 448 (1 for an all-zero block), codes = RNE of
+    x / scale (torch's float8_e4m3fn conversion).  Returns (codes uint8,
+    scales float32 with the leading axes)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    axes = tuple(range(x.ndim - nblock_axes, x.ndim))
+    amax = np.max(np.abs(x), axis=axes)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale.reshape(scale.shape + (1,) * nblock_axes)).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def prefill_inputs_fp8(w: Prefill, *, seed: Optional[int] = None):
+    """Return (q8, k8, v8, qscale, kscale, vscale) for the 8-bit forward.
+
+    q, k and v are drawn in fp32 exactly as ``prefill_inputs`` draws them
+    before rounding (q times its multiplier); q is stored with one scale per
+    row, k and v with one scale per (batch, kv head)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = _draw(rng, (w.B, w.Hq, w.Tq, w.d), "f32", w.q_mult)
+    k = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), "f32")
+    v = _draw(rng, (w.B, w.Hkv, w.Tk, w.d), "f32")
+    q8, qs = quantize_blocks_e4m3(q, 1)
+    k8, ks = quantize_blocks_e4m3(k, 2)
+    v8, vs = quantize_blocks_e4m3(v, 2)
+    return q8, k8, v8, qs, ks, vs

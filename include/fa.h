@@ -102,6 +102,31 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                void* stream);
 
 /*
+ * fa_fwd_fp8 -- fa_fwd over 8-bit inputs with block scales (the FP8 path of
+ * [LESSON] section "FlashAttention-2, -3 и дальше" and [FA3QA] section 6:
+ * E4M3 operands, higher-precision accumulation).
+ *
+ *   q      : [B, Hq,  Tq, d] uint8 E4M3 codes    qscale : [B, Hq, Tq] fp32
+ *   k, v   : [B, Hkv, Tk, d] uint8 E4M3 codes    kscale, vscale : [B, Hkv] fp32
+ *   o, lse : as fa_fwd (bf16, fp32)
+ * The inputs stand for q[b,h,i,:] = qscale[b,h,i] * e4m3(q8[b,h,i,:]) (one
+ * scale per query row, fixed by the whole row as in [BOOK5] section 5.4.3,
+ * Example 5-7), k[b,h,j,:] = kscale[b,h] * e4m3(k8[b,h,j,:]) and v alike
+ * (one scale per kv head).  Scales must be positive and finite.  Computes
+ * exactly what fa_fwd computes for those inputs (same causal modes 0/1/2,
+ * any finite scale), with this arithmetic: q.k products of the codes are
+ * exact and summed in fp32 on the 8-bit matrix cores; the online softmax is
+ * fp32; each probability, times 448, is rounded to E4M3 (relative error at
+ * most 2^-4, absolute at most 2^-10/448 near zero) for the p.v product,
+ * which sums in fp32; the row sum uses the unrounded probabilities; o is
+ * rounded to bf16.  Errors: as fa_fwd, and FA_ERR_NULL for a NULL scale
+ * array on a non-empty call.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* qscale,
+               const float* kscale, const float* vscale, void* o, float* lse, int B, int Hq,
+               int Hkv, int Tq, int Tk, int d, int causal, float scale, void* stream);
+
+/*
  * fa_bwd -- gradients of fa_fwd (training backward pass), bf16 in/out.
  *
  * Given the forward's inputs q, k, v, its output o and row log-sum-exp lse

@@ -25,6 +25,7 @@ from .attention import (  # noqa: F401
     decode_attention,
     decode_attention_fp8,
     e4m3_to_f64,
+    fp8_attention_inputs,
     decode_split_merge,
     online_normalizer,
     online_weighted_sum,

@@ -356,6 +356,23 @@ def e4m3_to_f64(codes) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, out)
 
 
+def fp8_attention_inputs(q8, k8, v8, qscale, kscale, vscale):
+    """Dequantise block-scaled E4M3 attention inputs to fp64.
+
+    q8:[B,Hq,Tq,d] with one scale per query row qscale:[B,Hq,Tq];
+    k8, v8:[B,Hkv,Tk,d] with one scale per (batch, kv head) kscale,
+    vscale:[B,Hkv] -- the FP8 forward path with block scaling ([LESSON]
+    section "FlashAttention-2, -3 и дальше"; a row's scale is fixed by the
+    whole row, [BOOK5] section 5.4.3, Example 5-7).  Returns (q, k, v) in
+    fp64; the attention of the 8-bit inputs is exactly the attention of
+    these.
+    """
+    q = e4m3_to_f64(q8) * np.asarray(qscale, np.float64)[..., None]
+    k = e4m3_to_f64(k8) * np.asarray(kscale, np.float64)[..., None, None]
+    v = e4m3_to_f64(v8) * np.asarray(vscale, np.float64)[..., None, None]
+    return q, k, v
+
+
 def decode_attention_fp8(q, kcodes, vcodes, kscale, vscale, seqlens) -> Tuple[np.ndarray, np.ndarray]:
     """Decode over an 8-bit cache: dequantize, then the decode definition.
 

@@ -138,3 +138,42 @@ def check_bounded(name, got, want, bound):
     print(f"  {name}: max|err| = {np.max(err):.3e}, max|ref| = {np.max(np.abs(want)):.3e}, "
           f"max err/bound = {ratio:.3f}", flush=True)
     assert ratio <= 1.0, f"{name}: error exceeds its bound (ratio {ratio:.3f})"
+
+
+# ---------------------------------------------------------------------------
+# 8-bit forward: element-wise error bound
+# ---------------------------------------------------------------------------
+E4M3_U = 2.0 ** -4            # relative rounding of an E4M3 normal value (3 mantissa bits)
+E4M3_FLOOR = 2.0 ** -10 / 448  # absolute rounding of 448 * P below the smallest normal, in P units
+
+
+def fp8_fwd_error_bound(q, k, v, *, causal, scale, causal_off=0, safety=1.25):
+    """Bound on |O_kernel - O_exact| for fa_fwd_fp8, element by element.
+
+    q, k, v: the dequantised fp64 inputs.  The only rounding of consequence
+    is that of each probability P_ij = exp(s_ij - m_i) <= 1 (times 448) to
+    E4M3 before the P.V product: |dP| <= max(2^-4 P, 2^-10/448).  With the
+    row sum l_i = sum_j P_ij unrounded,
+        |O_err[i, c]| <= sum_j max(2^-4 P_ij, 2^-10/448) |v_jc| / l_i,
+    plus the bf16 rounding of O (2^-8 |O|); times `safety`, plus 1e-6."""
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    bound = np.zeros((B, Hq, Tq, v.shape[3]))
+    O = np.zeros_like(bound)
+    i_idx = np.arange(Tq)[:, None]
+    j_idx = np.arange(Tk)[None, :]
+    vis = (j_idx <= i_idx + causal_off) if causal else np.ones((Tq, Tk), bool)
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            s = np.where(vis, scale * (q[b, h] @ k[b, kh].T), -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            P = np.where(vis, np.exp(s - m), 0.0)
+            l = P.sum(axis=1, keepdims=True)
+            lsafe = np.where(l > 0, l, 1.0)
+            dP = np.where(vis, np.maximum(E4M3_U * P, E4M3_FLOOR), 0.0)
+            bound[b, h] = (dP @ np.abs(v[b, kh])) / lsafe
+            O[b, h] = (P @ v[b, kh]) / lsafe
+    return safety * (bound + 2.0 ** -8 * np.abs(O)) + 1e-6

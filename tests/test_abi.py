@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_decode", "fa_strerror",
+    for n in ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_strerror",
               "fa_release_workspace", "fa_decode_workgroups", "fa_read_probe", "fa_decode_fp8",
               "fa_decode_fp8_workgroups"):
         assert n in names
@@ -67,6 +67,22 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 def test_fwd_validation(lib, entry, args, status):
     fn = getattr(lib, entry)
     assert fn(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, k, v, qs, ks, vs, o, lse, B, Hq, Hkv, Tq, Tk, d, causal, scale)
+    ((FAKE,) * 8 + (1, 4, 2, 8, 8, 96, 1, 0.1), 3),
+    ((FAKE,) * 8 + (1, 4, 3, 8, 8, 64, 1, 0.1), 2),
+    ((FAKE,) * 8 + (1, 4, 2, 8, 8, 64, 3, 0.1), 2),
+    ((FAKE,) * 8 + (1, 4, 2, 8, 8, 64, 1, float("inf")), 2),
+    ((FAKE, FAKE, FAKE, P, FAKE, FAKE, FAKE, P) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # qscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, P, FAKE, FAKE, P) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # kscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, P, FAKE, P) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # vscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, P, P) + (1, 4, 2, 8, 8, 64, 1, 0.1), 1),   # o NULL
+    ((P,) * 8 + (0, 4, 2, 8, 8, 64, 1, 0.1), 0),
+])
+def test_fwd_fp8_validation(lib, args, status):
+    assert lib.fa_fwd_fp8(*args, None) == status
 
 
 @pytest.mark.parametrize("args,status", [

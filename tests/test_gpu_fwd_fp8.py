@@ -1,0 +1,131 @@
+"""GPU parity of the 8-bit forward (fa_fwd_fp8: E4M3 q with per-row scales,
+E4M3 k and v with per-head scales) against the fp64 oracle on the
+dequantised inputs, through the C ABI.
+
+Bar (element-wise, derived from the kernel's arithmetic in
+gpu_helpers.fp8_fwd_error_bound): the probabilities are the one quantity
+rounded to 8 bits, so |O err| <= 1.25 * (sum_j max(2^-4 P_ij, 2^-10/448)
+|v_j| / l_i + 2^-8 |O_i|); lse <= 1e-3 (the scores are exact products).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from exact_tiled_attention_02_amd import inputs
+from gpu_helpers import BF16_LSE_TOL, check, fp8_fwd_error_bound, host_bf16_as_f64, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_tiled_attention_02_amd import fa
+    fa.load()
+
+
+def run_fp8(q8, k8, v8, qs, ks, vs, causal_mode, scale):
+    from exact_tiled_attention_02_amd import fa
+    B, Hq, Tq, d = q8.shape
+    _, Hkv, Tk, _ = k8.shape
+    t = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in (q8, k8, v8)]
+    s = [torch.from_numpy(np.ascontiguousarray(x, np.float32)).cuda() for x in (qs, ks, vs)]
+    o = torch.full((B, Hq, Tq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, Hq, Tq), float("nan"), dtype=torch.float32, device="cuda")
+    fa.fa_fwd_fp8(*t, *s, o, lse, B, Hq, Hkv, Tq, Tk, d, causal_mode, scale,
+                  torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return host_bf16_as_f64(o), host_f64(lse)
+
+
+def check_bounded(O, Or, bound):
+    err = np.abs(O - Or)
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    print(f"  O: max|err| = {np.max(err) if err.size else 0:.3e}, max err/bound = {ratio:.3f}",
+          flush=True)
+    assert np.all(np.isfinite(O)) and ratio <= 1.0
+
+
+def parity(w, align="top_left", scale=None):
+    sc = w.scale if scale is None else scale
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    mode = (2 if align == "bottom_right" else 1) if w.causal else 0
+    say("fa_fwd_fp8", w, align, sc)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, mode, sc)
+    q, k, v = oracle.fp8_attention_inputs(q8, k8, v8, qs, ks, vs)
+    Or, Lr = oracle.softmax_attention(q, k, v, causal=w.causal, scale=sc, align=align)
+    bound = fp8_fwd_error_bound(q, k, v, causal=w.causal, scale=sc,
+                                causal_off=oracle.causal_offset(w.Tq, w.Tk, align))
+    check_bounded(O, Or, bound)
+    check("lse", L, Lr, BF16_LSE_TOL)
+    return O, L
+
+
+SMALL = [
+    # B, Hq, Hkv, Tq, Tk, d, causal
+    (1, 1, 1, 1, 1, 64, False),
+    (1, 1, 1, 1, 1, 128, True),
+    (1, 2, 1, 7, 7, 64, True),
+    (1, 1, 1, 13, 13, 128, False),
+    (2, 4, 2, 100, 100, 64, True),
+    (1, 8, 2, 257, 257, 128, True),
+    (1, 4, 4, 130, 70, 64, False),
+    (1, 4, 1, 65, 200, 128, True),
+    (1, 2, 2, 200, 65, 64, True),
+    (2, 6, 3, 300, 300, 128, True),
+    (1, 6, 2, 100, 100, 64, True),
+    (1, 8, 1, 70, 70, 128, True),
+    (1, 2, 2, 128, 128, 128, False),
+    (1, 1, 1, 383, 383, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_fp8_small_shapes(shape):
+    B, Hq, Hkv, Tq, Tk, d, causal = shape
+    parity(inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=causal, seed=41))
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 2, 70, 300, 128), (1, 2, 2, 200, 65, 64)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_fp8_bottom_right(shape):
+    B, Hq, Hkv, Tq, Tk, d = shape
+    parity(inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=Tq, Tk=Tk, d=d, causal=True, seed=42),
+           align="bottom_right")
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+def test_fp8_other_scales(scale):
+    parity(inputs.Prefill("t", B=1, Hq=2, Hkv=1, Tq=150, Tk=150, d=64, causal=True, seed=43),
+           scale=scale)
+
+
+def test_fp8_peaked_rows():
+    """Q x 3 (the Qwen3-shaped workload's distribution)."""
+    parity(inputs.Prefill("t", B=1, Hq=4, Hkv=2, Tq=300, Tk=300, d=128, causal=True, q_mult=3.0,
+                          seed=44))
+
+
+def test_fp8_qwen3_shape_full():
+    """Hq=16, Hkv=8, T=4096, d=128, causal, Q x 3 in 8 bits: every element."""
+    w = inputs.Prefill("qwen3 fp8", B=1, Hq=16, Hkv=8, Tq=4096, Tk=4096, d=128, causal=True,
+                       q_mult=3.0)
+    parity(w)
+
+
+def test_fp8_gpt2_shape_sampled():
+    """B=8, H=12, T=4096, d=64 causal in 8 bits: full launch; two (batch,
+    head) pairs checked in full."""
+    w = inputs.Prefill("gpt2 fp8", B=8, Hq=12, Hkv=12, Tq=4096, Tk=4096, d=64, causal=True)
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    say("fa_fwd_fp8", w.name)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
+    for b, h in ((0, 0), (7, 11)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        q, k, v = oracle.fp8_attention_inputs(q8[sl], k8[sl], v8[sl], qs[sl], ks[sl], vs[sl])
+        Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
+        check_bounded(O[sl], Or, fp8_fwd_error_bound(q, k, v, causal=True, scale=w.scale))
+        check("lse", L[sl], Lr, BF16_LSE_TOL)

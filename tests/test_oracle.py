@@ -724,3 +724,23 @@ def test_fp8_row_quantisation_uses_the_full_range():
     assert np.all(np.max(np.abs(vals), axis=-1) == 448.0)
     rel = np.abs(vals * sc[..., None] - x) / np.max(np.abs(x), axis=-1, keepdims=True)
     assert np.max(rel) <= 16 / 448   # half the E4M3 spacing (32) of the top binade, relative to amax
+
+
+def test_fp8_attention_inputs_dequantise_with_torch():
+    """Library routine: torch's E4M3 widening times the block scales (per
+    query row; per batch and kv head for k and v)."""
+    torch = pytest.importorskip("torch")
+    w = inputs.Prefill("t", B=2, Hq=4, Hkv=2, Tq=9, Tk=11, d=16, causal=True, q_mult=3.0, seed=40)
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    q, k, v = oracle.fp8_attention_inputs(q8, k8, v8, qs, ks, vs)
+    wid = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()  # noqa: E731
+    assert np.array_equal(q, wid(q8) * qs[..., None])
+    assert np.array_equal(k, wid(k8) * ks[:, :, None, None])
+    assert np.array_equal(v, wid(v8) * vs[:, :, None, None])
+    # Block scaling: each block's largest code is +-448.
+    assert np.all(np.max(np.abs(wid(q8)), axis=-1) == 448)
+    assert np.all(np.max(np.abs(wid(k8)), axis=(-1, -2)) == 448)
+    # The stored values reproduce the fp32 draw within half an E4M3 step.
+    rng = np.random.default_rng(40)
+    qf = rng.standard_normal((2, 4, 9, 16), dtype=np.float32) * np.float32(3.0)
+    assert np.max(np.abs(q - qf) / np.max(np.abs(qf), axis=-1, keepdims=True)) <= 16 / 448
