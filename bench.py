@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 matrix-core peak (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 matrix-core peak (twice the bf16 rate)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources each workload's kernels are built from: a traffic figure counts
 # only while they are unchanged since the counters were taken.
@@ -116,12 +117,32 @@ def time_calls(torch, launch, steps: int, warmup: int):
 def prefill_case(torch, fa, w, steps, warmup, seed=0):
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
+    stream = torch.cuda.current_stream()
+    lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
+    if w.dtype == "fp8":
+        # fp32 N(0,1) draws stored as E4M3 codes with block scales: one per
+        # query row, one per (batch, kv head) for k and v.
+        def quant(x, dims):
+            sc = x.abs().amax(dim=dims, keepdim=True) / 448.0
+            return (x / sc).to(torch.float8_e4m3fn).view(torch.uint8), sc.reshape(
+                [n for i, n in enumerate(x.shape) if i - x.dim() not in dims]).contiguous()
+        qf = torch.randn((w.B, w.Hq, w.Tq, w.d), generator=gen, device="cuda") * w.q_mult
+        kf = torch.randn((w.B, w.Hkv, w.Tk, w.d), generator=gen, device="cuda")
+        vf = torch.randn((w.B, w.Hkv, w.Tk, w.d), generator=gen, device="cuda")
+        q, qs = quant(qf, (-1,))
+        k, ks = quant(kf, (-2, -1))
+        v, vs = quant(vf, (-2, -1))
+        del qf, kf, vf
+        o = torch.empty((w.B, w.Hq, w.Tq, w.d), dtype=torch.bfloat16, device="cuda")
+        launch = fa.prepared("fa_fwd_fp8", q, k, v, qs, ks, vs, o, lse, w.B, w.Hq, w.Hkv, w.Tq,
+                             w.Tk, w.d, w.causal_mode, w.scale, stream=stream)
+        wall, ev_ms = time_calls(torch, launch, steps, warmup)
+        del q, k, v, qs, ks, vs, o, lse
+        return wall, ev_ms
     q = dev_normal(torch, (w.B, w.Hq, w.Tq, w.d), gen, w.q_mult)
     k = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
     v = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.Tq), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
 
     launch = fa.prepared("fa_fwd", q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d,
                          w.causal_mode, w.scale, stream=stream)
@@ -288,7 +309,9 @@ def run_only(torch, fa, inputs, args):
     if isinstance(w, inputs.Prefill):
         wall, ev = prefill_case(torch, fa, w, args.steps, args.warmup)
         out = {"workload": w.name, "TFLOP/s": round(w.flops / wall / 1e12, 2),
-               "kernel_ms": round(ev, 4), "frac_of_mfma_peak": round(w.flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+               "kernel_ms": round(ev, 4),
+               "frac_of_mfma_peak": round(w.flops / (ev * 1e-3) / 1e12 /
+                                          (PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS), 4)}
     else:
         wall, ev, nbytes, _ = decode_case(torch, fa, w, args.steps, args.warmup, args.decode_splits)
         out = {"workload": w.name, "GB/s": round(nbytes / (ev * 1e-3) / 1e9, 1),
@@ -358,14 +381,18 @@ def main():
     if not args.no_extra:
         also = {}
         for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 10),
-                            ("llama3_8b_chunk", 20)):
+                            ("llama3_8b_chunk", 20), ("gpt2_small_mha_fp8", max(10, args.steps)),
+                            ("qwen3_0p6b_gqa_fp8", max(10, args.steps)),
+                            ("llama3_8b_long_fp8", 10)):
             wk = inputs.WORKLOADS[name]
             log(f"[bench] {wk.name}")
             wl, ev = prefill_case(torch, fa, wk, steps, max(2, min(args.warmup, steps)))
             ach = wk.flops / (ev * 1e-3) / 1e12
+            peak = PEAK_FP8_TFLOPS if wk.dtype == "fp8" else PEAK_BF16_TFLOPS
             also[name] = {"value": round(wk.flops / wl / 1e12, 2), "unit": "TFLOP/s",
                           "ms_per_call": round(wl * 1e3, 4), "kernel_ms": round(ev, 4),
-                          "frac_of_mfma_peak": round(ach / PEAK_BF16_TFLOPS, 4),
+                          "frac_of_mfma_peak": round(ach / peak, 4),
+                          "mfma_peak": peak, "dtype": wk.dtype,
                           "traffic": measured_traffic(name)}
             log(f"[bench]   {also[name]}")
         for name, steps in (("gpt2_small_mha", 20), ("qwen3_0p6b_gqa", 20), ("llama3_8b_long", 3)):

@@ -66,7 +66,7 @@ class Prefill:
     Tk: int
     d: int
     causal: bool
-    dtype: str = "bf16"          # "bf16" or "f32"
+    dtype: str = "bf16"          # "bf16", "f32", or "fp8" (E4M3 with block scales)
     q_mult: float = 1.0
     seed: int = 0
     align: str = "top_left"      # causal diagonal: "top_left" or "bottom_right"
@@ -149,6 +149,15 @@ LLAMA3_8B_CHUNK = Prefill("Llama-3-8B GQA chunked prefill, last 4096 of 32768 po
                           "(bottom-right causal), Hq=32, Hkv=8, d=128",
                           B=1, Hq=32, Hkv=8, Tq=4096, Tk=32768, d=128, causal=True,
                           align="bottom_right")
+GPT2_SMALL_MHA_FP8 = Prefill("GPT-2-small MHA causal prefill in 8 bits (E4M3 q per-row, k/v "
+                             "per-head scales), B=8, H=12, T=4096, d=64",
+                             B=8, Hq=12, Hkv=12, Tq=4096, Tk=4096, d=64, causal=True, dtype="fp8")
+QWEN3_0P6B_GQA_FP8 = Prefill("Qwen3-0.6B GQA causal prefill in 8 bits, Hq=16, Hkv=8, T=4096, "
+                             "d=128, Qx3", B=1, Hq=16, Hkv=8, Tq=4096, Tk=4096, d=128, causal=True,
+                             q_mult=3.0, dtype="fp8")
+LLAMA3_8B_LONG_FP8 = Prefill("Llama-3-8B GQA causal prefill in 8 bits, Hq=32, Hkv=8, T=32768, "
+                             "d=128", B=1, Hq=32, Hkv=8, Tq=32768, Tk=32768, d=128, causal=True,
+                             dtype="fp8")
 FLASH_DECODE = Decode("split-KV decode, B=16, Hq=32, Hkv=8, d=128, seqlen U[1024,32768]",
                       B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768)
 
@@ -163,6 +172,9 @@ WORKLOADS = {
     "qwen3_0p6b_gqa": QWEN3_0P6B_GQA,
     "llama3_8b_long": LLAMA3_8B_LONG,
     "llama3_8b_chunk": LLAMA3_8B_CHUNK,
+    "gpt2_small_mha_fp8": GPT2_SMALL_MHA_FP8,
+    "qwen3_0p6b_gqa_fp8": QWEN3_0P6B_GQA_FP8,
+    "llama3_8b_long_fp8": LLAMA3_8B_LONG_FP8,
     "flash_decode": FLASH_DECODE,
     "flash_decode_fp8": FLASH_DECODE_FP8,
 }
