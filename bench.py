@@ -44,6 +44,10 @@ KERNEL_SOURCES = {
                 "exact_tiled_attention_02_amd/csrc/fa_device.h",
                 "exact_tiled_attention_02_amd/csrc/fa_lds.h",
                 "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
+    "prefill_fp8": ["exact_tiled_attention_02_amd/csrc/fa_fwd_fp8.hip",
+                    "exact_tiled_attention_02_amd/csrc/fa_device.h",
+                    "exact_tiled_attention_02_amd/csrc/fa_lds.h",
+                    "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
     "decode": ["exact_tiled_attention_02_amd/csrc/fa_decode.hip",
                "exact_tiled_attention_02_amd/csrc/fa_device.h",
                "exact_tiled_attention_02_amd/csrc/fa_launch.h"],
@@ -76,7 +80,9 @@ def measured_traffic(workload: str):
     if w is None:
         return None
     from exact_tiled_attention_02_amd import inputs
-    kind = "decode" if isinstance(inputs.WORKLOADS[workload], inputs.Decode) else "prefill"
+    wk = inputs.WORKLOADS[workload]
+    kind = ("decode" if isinstance(wk, inputs.Decode)
+            else "prefill_fp8" if wk.dtype == "fp8" else "prefill")
     if w.get("kernel_source_hash") != kernel_source_hash(kind):
         return None
     return w.get("hbm_bytes_per_launch")

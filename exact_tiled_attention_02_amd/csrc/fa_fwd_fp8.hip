@@ -55,10 +55,12 @@ constexpr float kLog2E4M3Max = 8.807354922057604f;   // log2(448)
 // separate rows sharing an LDS bank line (1..3 at 128-byte rows, 2..3 at
 // 64-byte rows): 16 consecutive rows read at one chunk hit distinct banks,
 // and so do the 8 rows {0..3, 8..11} (+4) that one transposing read
-// gathers.  Rows r and r + 16i get the same value.
+// gathers, also together with the neighbouring 16-lane group that reads the
+// adjacent chunk (at 128-byte rows those rows get even or odd values only).
+// Rows r and r + 16i get the same value.
 template <int D>
 __device__ __forceinline__ int f8swz(int r) {
-  return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+  return D == 128 ? ((((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | ((r >> 2) & 1)) : ((r >> 2) & 3);
 }
 
 // 32x32x64 MFMA on E4M3 operands with unit block scales.

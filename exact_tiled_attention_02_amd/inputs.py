@@ -103,11 +103,17 @@ class Prefill:
 
     @property
     def min_bytes(self) -> int:
-        """Bytes that must cross HBM once: q, k, v read; o, lse written."""
+        """Bytes that must cross HBM once: q, k, v read; o, lse written (8-bit
+        inputs: the codes and their scales read, o written in bf16)."""
+        rows = self.B * self.Hq * self.Tq
+        if self.dtype == "fp8":
+            q = rows * (self.d + 4)
+            kv = 2 * self.B * self.Hkv * (self.Tk * self.d + 4)
+            return q + kv + rows * self.d * 2 + rows * 4
         es = 2 if self.dtype == "bf16" else 4
-        q = self.B * self.Hq * self.Tq * self.d * es
+        q = rows * self.d * es
         kv = 2 * self.B * self.Hkv * self.Tk * self.d * es
-        return 2 * q + kv + self.B * self.Hq * self.Tq * 4
+        return 2 * q + kv + rows * 4
 
 
 @dataclasses.dataclass(frozen=True)
