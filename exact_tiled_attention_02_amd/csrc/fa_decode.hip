@@ -193,15 +193,15 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
       for (int u = 0; u < KU; ++u) {
         const int key = k0 + u * RPW;
         const bool in = key < hi;
-        kb[u] = in ? *(const raw_t*)(Kg8 + (size_t)key * D + dl * EPL) : raw_t{};
-        ks[u] = in ? p.kscale[srow + key] : 0.f;
+        kb[u] = in ? stream_load((const raw_t*)(Kg8 + (size_t)key * D + dl * EPL)) : raw_t{};
+        ks[u] = in ? stream_load(p.kscale + srow + key) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int key = k0 + u * RPW;
         const bool in = key < hi;
-        vb[u] = in ? *(const raw_t*)(Vg8 + (size_t)key * D + dl * EPL) : raw_t{};
-        vs[u] = in ? p.vscale[srow + key] : 0.f;
+        vb[u] = in ? stream_load((const raw_t*)(Vg8 + (size_t)key * D + dl * EPL)) : raw_t{};
+        vs[u] = in ? stream_load(p.vscale + srow + key) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < KU; ++u)
@@ -216,14 +216,14 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
         const int key = k0 + u * RPW;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          kr[u][j] = key < hi ? *(const u32x4*)(Kg + (size_t)key * D + eoff(j)) : zero;
+          kr[u][j] = key < hi ? stream_load((const u32x4*)(Kg + (size_t)key * D + eoff(j))) : zero;
       }
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int key = k0 + u * RPW;
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          vr[u][j] = key < hi ? *(const u32x4*)(Vg + (size_t)key * D + eoff(j)) : zero;
+          vr[u][j] = key < hi ? stream_load((const u32x4*)(Vg + (size_t)key * D + eoff(j))) : zero;
       }
     }
 

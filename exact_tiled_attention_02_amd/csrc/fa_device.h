@@ -25,6 +25,15 @@ constexpr float kNegInf = -__builtin_inff();
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Streaming load: a nontemporal global load (the "nt" cache policy), for
+// data that is read exactly once.  On gfx950 a contiguous 16-byte-per-lane
+// stream of such loads reaches about 7 TB/s, against 6.0-6.4 TB/s for the
+// same stream with the default policy.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+  return __builtin_nontemporal_load(p);
+}
+
 // Value of lane (lane ^ 32): the two halves of a wavefront trade values.
 __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);

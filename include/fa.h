@@ -250,7 +250,8 @@ int fa_decode_fp8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_
 /*
  * fa_read_probe -- measurement utility, not part of the attention path:
  * reads `bytes` bytes of device memory at `src` exactly once with 16-byte
- * loads (one 1 MiB chunk per workgroup, several loads in flight per lane)
+ * nontemporal loads (one 1 MiB chunk per workgroup, several loads in flight
+ * per lane)
  * and XORs every 32-bit word into *sink (device memory, zeroed by the
  * caller), so that a caller can time the device's achievable read
  * bandwidth and report it beside fa_decode's, whose workload is a single
