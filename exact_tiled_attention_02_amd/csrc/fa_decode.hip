@@ -102,6 +102,15 @@ __device__ __forceinline__ uint32_t bf16_pair_bits(float a, float b) {
   return w;
 }
 
+// a.x * b.x + a.y * b.y in fp32 (bf16 pairs).  The three-operand form with
+// an inline zero addend starts a dot chain without first zeroing the
+// accumulator register, which the two-operand form would need.
+__device__ __forceinline__ float dot2_from_zero(bf16x2 a, bf16x2 b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Elements held by a lane: EPL = 8 * NV values, vector j (16 bytes) being
 // elements [j * d / NV + dl * 8, +8) of the row, dl = lane % LPR.
 template <int D, int HPW>
@@ -144,6 +153,13 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, NV = S::NV;
   constexpr int STEP = 4 * RPW * KU;   // keys per workgroup iteration
   static_assert(KU % 2 == 0, "keys are paired within a lane");
+  // The range is the same for the whole workgroup; keep it in scalar
+  // registers so that the buffer resources built from it are scalar too.
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  hq0 = __builtin_amdgcn_readfirstlane(hq0);
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -164,11 +180,10 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
       qv[h][j] = *(const u32x4*)((const bf16*)p.q + ((size_t)b * p.Hq + hq0 + h) * D + eoff(j));
 
   const size_t head_off = ((size_t)b * p.Hkv + kvh) * p.Tk_max * D;
-  const bf16* Kg = (const bf16*)p.kcache + head_off;
-  const bf16* Vg = (const bf16*)p.vcache + head_off;
-  const uint8_t* Kg8 = (const uint8_t*)p.kcache + head_off;
-  const uint8_t* Vg8 = (const uint8_t*)p.vcache + head_off;
   const size_t srow = ((size_t)b * p.Hkv + kvh) * p.Tk_max;   // row-scale index of key 0
+  constexpr int ESZ = FP8 ? 1 : 2;                           // bytes per cache element
+  const char* Kb = (const char*)p.kcache + head_off * ESZ;
+  const char* Vb = (const char*)p.vcache + head_off * ESZ;
 
   float m[HPW], l[HPW], o[HPW][EPL];
 #pragma unroll
@@ -178,30 +193,48 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
   }
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+
+  // Loads go through buffer resources based at the iteration's first key
+  // whose size ends at key hi: a row at or past hi reads zeros (its score
+  // is masked below), with no branch per load.  The per-lane byte offsets
+  // inside an iteration are loop invariants.  Cache rows are streamed with
+  // the nontemporal policy (read exactly once).
+  constexpr int kNT = 2;   // buffer-load cache policy: nt
+  uint32_t roff[KU];       // row of load step u inside the iteration
+#pragma unroll
+  for (int u = 0; u < KU; ++u) roff[u] = (uint32_t)(wave * RPW * KU + u * RPW + row);
 
   for (int base = lo; base < hi; base += STEP) {
-    // Key of load step u of this lane: k0 + u * RPW.
+    const uint32_t rows_left = (uint32_t)min(hi - base, STEP);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kb + (size_t)base * D * ESZ), 0, rows_left * D * ESZ, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vb + (size_t)base * D * ESZ), 0, rows_left * D * ESZ, 0x00020000);
+    // Key of load step u of this lane: base + roff[u].
     const int k0 = base + wave * RPW * KU + row;
     u32x4 kr[KU][NV], vr[KU][NV];
     float ks[KU], vs[KU];   // FP8: row scales (0 past the range)
     if constexpr (FP8) {
+      const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.kscale + srow + base), 0, rows_left * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.vscale + srow + base), 0, rows_left * 4, 0x00020000);
       // EPL codes per lane: one 16- or 8-byte load per row and tensor.
       typedef uint32_t raw_t __attribute__((ext_vector_type(EPL / 4)));
       raw_t kb[KU], vb[KU];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const int key = k0 + u * RPW;
-        const bool in = key < hi;
-        kb[u] = in ? stream_load((const raw_t*)(Kg8 + (size_t)key * D + dl * EPL)) : raw_t{};
-        ks[u] = in ? stream_load(p.kscale + srow + key) : 0.f;
+        const uint32_t off = roff[u] * D + dl * EPL;
+        if constexpr (EPL == 16) kb[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, kNT);
+        else kb[u] = __builtin_amdgcn_raw_buffer_load_b64(krs, off, 0, kNT);
+        ks[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ksr, roff[u] * 4, 0, kNT));
       }
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const int key = k0 + u * RPW;
-        const bool in = key < hi;
-        vb[u] = in ? stream_load((const raw_t*)(Vg8 + (size_t)key * D + dl * EPL)) : raw_t{};
-        vs[u] = in ? stream_load(p.vscale + srow + key) : 0.f;
+        const uint32_t off = roff[u] * D + dl * EPL;
+        if constexpr (EPL == 16) vb[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kNT);
+        else vb[u] = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kNT);
+        vs[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, roff[u] * 4, 0, kNT));
       }
 #pragma unroll
       for (int u = 0; u < KU; ++u)
@@ -212,19 +245,15 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
         }
     } else {
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        const int key = k0 + u * RPW;
+      for (int u = 0; u < KU; ++u)
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          kr[u][j] = key < hi ? stream_load((const u32x4*)(Kg + (size_t)key * D + eoff(j))) : zero;
-      }
+          kr[u][j] = __builtin_amdgcn_raw_buffer_load_b128(krs, (roff[u] * D + eoff(j)) * 2, 0, kNT);
 #pragma unroll
-      for (int u = 0; u < KU; ++u) {
-        const int key = k0 + u * RPW;
+      for (int u = 0; u < KU; ++u)
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          vr[u][j] = key < hi ? stream_load((const u32x4*)(Vg + (size_t)key * D + eoff(j))) : zero;
-      }
+          vr[u][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (roff[u] * D + eoff(j)) * 2, 0, kNT);
     }
 
     // Scores, reduced over the LPR lanes of each row.
@@ -233,11 +262,11 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
     for (int u = 0; u < KU; ++u)
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
-        float acc = 0.f;
+        float acc = dot2_from_zero(as_bf16x2(kr[u][0][0]), as_bf16x2(qv[h][0][0]));
 #pragma unroll
         for (int j = 0; j < NV; ++j)
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
+          for (int w = j == 0 ? 1 : 0; w < 4; ++w)
             acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][j][w]), as_bf16x2(qv[h][j][w]),
                                                   acc, false);
         sc[u][h] = LPR == 8 ? group8_sum(acc) : group16_sum(acc);
