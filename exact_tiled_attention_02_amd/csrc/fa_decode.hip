@@ -45,11 +45,15 @@
 //    (lane shuffles), then the 4 wavefronts through LDS, and the piece's
 //    (m, l, o) is written to the workspace.
 // An 8-bit cache (E4M3 codes, one fp32 scale per row: [NOTE]'s fused
-// dequantisation, the cache expanded inside the tile load) runs the same
-// loop: the codes are widened to bf16 in registers right after the load.
+// dequantisation, the cache expanded inside the tile load) widens the codes
+// to bf16 in registers right after the load.  At d = 128 with 4 or 8 heads
+// per workgroup it runs a matrix-core loop (decode_range_mfma): the scores
+// and P.V on the 16x16x32 bf16 matrix core, V^T through LDS; otherwise the
+// packed-dot loop above.
 // Merge kernel, one wavefront per (sequence, query head): fixed-order pass
 // over the pieces, O = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.
 #include "fa_device.h"
+#include "fa_lds.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -214,14 +218,15 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
     const int k0 = base + wave * RPW * KU + row;
     u32x4 kr[KU][NV], vr[KU][NV];
     float ks[KU], vs[KU];   // FP8: row scales (0 past the range)
+    // FP8: EPL codes per lane and row, widened to bf16 only where used.
+    typedef uint32_t raw_t __attribute__((ext_vector_type(EPL / 4)));
+    raw_t kb[KU], vb[KU];
     if constexpr (FP8) {
       const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.kscale + srow + base), 0, rows_left * 4, 0x00020000);
       const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(p.vscale + srow + base), 0, rows_left * 4, 0x00020000);
       // EPL codes per lane: one 16- or 8-byte load per row and tensor.
-      typedef uint32_t raw_t __attribute__((ext_vector_type(EPL / 4)));
-      raw_t kb[KU], vb[KU];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
         const uint32_t off = roff[u] * D + dl * EPL;
@@ -236,13 +241,6 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
         else vb[u] = __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kNT);
         vs[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vsr, roff[u] * 4, 0, kNT));
       }
-#pragma unroll
-      for (int u = 0; u < KU; ++u)
-#pragma unroll
-        for (int j = 0; j < NV; ++j) {
-          kr[u][j] = e4m3x8_to_bf16(kb[u][2 * j], kb[u][2 * j + 1]);
-          vr[u][j] = e4m3x8_to_bf16(vb[u][2 * j], vb[u][2 * j + 1]);
-        }
     } else {
 #pragma unroll
       for (int u = 0; u < KU; ++u)
@@ -256,22 +254,31 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
           vr[u][j] = __builtin_amdgcn_raw_buffer_load_b128(vrs, (roff[u] * D + eoff(j)) * 2, 0, kNT);
     }
 
-    // Scores, reduced over the LPR lanes of each row.
+    // Scores, reduced over the LPR lanes of each row.  FP8: each 16-byte
+    // chunk of K is widened right where the HPW dot chains consume it, so
+    // that the widened row is never held whole.
     float sc[KU][HPW];
 #pragma unroll
-    for (int u = 0; u < KU; ++u)
+    for (int u = 0; u < KU; ++u) {
+      float acc[HPW];
 #pragma unroll
-      for (int h = 0; h < HPW; ++h) {
-        float acc = dot2_from_zero(as_bf16x2(kr[u][0][0]), as_bf16x2(qv[h][0][0]));
+      for (int j = 0; j < NV; ++j) {
+        const u32x4 k4 = FP8 ? e4m3x8_to_bf16(kb[u][2 * j], kb[u][2 * j + 1]) : kr[u][j];
 #pragma unroll
-        for (int j = 0; j < NV; ++j)
+        for (int h = 0; h < HPW; ++h) {
+          if (j == 0) acc[h] = dot2_from_zero(as_bf16x2(k4[0]), as_bf16x2(qv[h][0][0]));
 #pragma unroll
           for (int w = j == 0 ? 1 : 0; w < 4; ++w)
-            acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kr[u][j][w]), as_bf16x2(qv[h][j][w]),
-                                                  acc, false);
-        sc[u][h] = LPR == 8 ? group8_sum(acc) : group16_sum(acc);
+            acc[h] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(k4[w]), as_bf16x2(qv[h][j][w]),
+                                                     acc[h], false);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        sc[u][h] = LPR == 8 ? group8_sum(acc[h]) : group16_sum(acc[h]);
         if constexpr (FP8) sc[u][h] *= ks[u];
       }
+    }
     if (base + STEP > hi) {   // last iteration: keys past the range get -inf
 #pragma unroll
       for (int u = 0; u < KU; ++u)
@@ -314,6 +321,29 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
     }
 
     // O += P V, two keys per packed dot.
+    if constexpr (FP8) {
+      // Byte-interleave the codes of the two keys first (a0 b0 a1 b1 and
+      // a2 b2 a3 b3), so that each widening gives a (v_a, v_b) pair of one
+      // element directly.
+#pragma unroll
+      for (int t = 0; t < KU / 2; ++t)
+#pragma unroll
+        for (int i = 0; i < EPL / 4; ++i) {
+          const uint32_t wa = vb[2 * t][i], wb = vb[2 * t + 1][i];
+          const uint32_t x0 = __builtin_amdgcn_perm(wb, wa, 0x05010400u);
+          const uint32_t x1 = __builtin_amdgcn_perm(wb, wa, 0x07030602u);
+          const bf16x2 v2[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true)};
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int h = 0; h < HPW; ++h)
+              o[h][4 * i + k] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(pp[t][h]), v2[k],
+                                                                o[h][4 * i + k], false);
+        }
+    } else {
 #pragma unroll
     for (int t = 0; t < KU / 2; ++t)
 #pragma unroll
@@ -331,6 +361,7 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
             o[h][e + 1] = __builtin_amdgcn_fdot2_f32_bf16(ph, hi2, o[h][e + 1], false);
           }
         }
+    }
   }
 
   // Merge the rows of the wavefront (rescale rule), then hand the wavefront
@@ -381,6 +412,303 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
   __syncthreads();   // LDS is reused by the next range
 }
 
+// ---- Matrix-core loop for the E4M3 cache: d = 128, 4 or 8 heads per workgroup ----
+//
+// With one byte per cached element the packed-dot loop above spends more
+// vector instructions per byte than the memory time covers, so the 8-bit
+// cache takes this loop instead.  A wavefront takes blocks of 32
+// consecutive keys.  The scores of a block come from the 16x16x32 bf16
+// matrix core, S' = K Q^T, with the 16 keys of a half-block as rows and the
+// workgroup's query heads as columns: lane l then holds the scores of keys
+// 4*(l/16) + 0..3 of both half-blocks for head l % 16, which is exactly the
+// operand layout that O^T += V^T P^T takes for its probabilities, so no
+// lane exchange sits between the two products.  V^T (keys packed per lane)
+// is gathered from a per-wavefront LDS copy of the block with the gfx950
+// 8-bit transposing read.  The online softmax runs on 8 scores per lane,
+// with one running max per head shared by the four lane groups.  (The bf16
+// cache measured 1% faster on the packed-dot loop and stays there.)
+constexpr int kMB = 32;   // keys per wavefront block
+constexpr int kMfRowB = 128;   // bytes per cached E4M3 row at d = 128
+
+// First head-dimension index of the 8 elements that lane group grp holds in
+// k-step kk (four k-steps of 32 cover d = 128).  Any permutation works as
+// long as K and Q use the same one; this one lets each 16-byte K load serve
+// two k-steps.
+__device__ __forceinline__ int mf_dim0(int grp, int kk) {
+  return 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1);
+}
+// LDS swizzle of the 16-byte chunks of V row `row`: within 32 lanes, the 8
+// bytes of every lane of a transposing read fall in distinct banks.
+__device__ __forceinline__ int mf_vswz(int row) {
+  return ((row >> 1) & 1) | (((row >> 4) & 1) << 1) | (((row >> 2) & 1) << 2);
+}
+__device__ __forceinline__ f32x4 mma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// Max / sum over the four lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float groups_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float groups_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Same contract as decode_range_keys for the E4M3 cache (d = 128, HPW of 4
+// or 8); `vlds` holds 2 * 4 * kMB rows (two blocks per wavefront).
+template <int HPW>
+__device__ __forceinline__ void decode_range_mfma(const DecodeParams& p, int b, int kvh, int hq0,
+                                                  int lo, int hi, size_t slot, float (*red_m)[HPW],
+                                                  float (*red_l)[HPW], float (*red_o)[HPW][128],
+                                                  uint8_t* vlds) {
+  constexpr int D = 128;
+  constexpr int ROWB = kMfRowB;
+  constexpr int STEP = 4 * kMB;                 // keys per workgroup iteration
+  constexpr int NCOPY = kMB * ROWB / 1024;      // 1 KiB LDS copies per block
+  constexpr int RPC = 1024 / ROWB;              // rows per copy instruction
+  constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+  constexpr int kNT = 2;                        // buffer-load cache policy: nt
+  static_assert(HPW == 4 || HPW == 8, "matrix-core decode takes 4 or 8 heads");
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  hq0 = __builtin_amdgcn_readfirstlane(hq0);
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;    // head column (>= HPW: unused)
+  const int grp = lane >> 4;    // lane group
+  const float c = p.c;
+
+  // Q as the B operand of S' = K Q^T: qb[kk] = q[hq0 + col][mf_dim0(grp, kk) .. +8].
+  bf16x8 qb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (col < HPW)
+      w = *(const u32x4*)((const bf16*)p.q + ((size_t)b * p.Hq + hq0 + col) * D + mf_dim0(grp, kk));
+    __builtin_memcpy(&qb[kk], &w, sizeof(w));
+  }
+
+  const size_t row0 = ((size_t)b * p.Hkv + kvh) * p.Tk_max;   // cache row of key 0
+  const uint8_t* Kb = (const uint8_t*)p.kcache + row0 * ROWB;
+  const uint8_t* Vb = (const uint8_t*)p.vcache + row0 * ROWB;
+  uint8_t* vbuf = vlds + __builtin_amdgcn_readfirstlane(wave) * 2 * kMB * ROWB;
+
+  // Loop-invariant offsets, relative to the first key of a workgroup step.
+  // K: lane (col, grp) loads 16-byte chunks grp and 4 + grp of row
+  // kMB*wave + 16*hb + col.
+  const uint32_t koff = (uint32_t)((kMB * wave + col) * ROWB + 16 * grp);
+  // Row scales: lane (grp, n) loads the scale of key kappa(grp, n % 8) =
+  // 16*(n%8/4) + 4*grp + n%4 of the block (one coalesced 4-byte load per
+  // tensor and block, every key range-checked alone); each lane then takes
+  // the 8 values of its row by broadcast within the row.
+  const uint32_t soff = (uint32_t)((kMB * wave + 16 * ((lane & 7) >> 2) + 4 * grp + (lane & 3)) * 4);
+  // V copies: instruction n puts rows RPC*n .. into LDS, lane -> (row, chunk').
+  uint32_t vsrc[NCOPY];
+#pragma unroll
+  for (int n = 0; n < NCOPY; ++n) {
+    const int row = RPC * n + lane / CPR;
+    const int chunk = (lane % CPR) ^ mf_vswz(row);
+    vsrc[n] = (uint32_t)((kMB * wave + row) * ROWB + 16 * chunk);
+  }
+  // Transposing reads of V^T (ds_read_b64_tr_b8), one address per 16-dim
+  // block db: input lane 2e + h of a group addresses row
+  // kappa(grp, e) = 16*(e/4) + 4*grp + e%4, bytes 16*db + 8*h .. +8.
+  uint32_t vaddr[8];
+  {
+    const int gl = lane & 15;
+    const int e = gl >> 1, h = gl & 1;
+    const int row = 16 * (e >> 2) + 4 * grp + (e & 3);
+    const uint32_t vb0 = lds_addr(vbuf);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) vaddr[db] = vb0 + row * ROWB + 16 * (db ^ mf_vswz(row)) + 8 * h;
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Two blocks in flight per wavefront: the loads of the next block (K rows
+  // into registers, row scales, V rows into the other LDS buffer) are issued
+  // before the current block is computed.
+  u32x4 kc[2][2][2];
+  uint32_t ksr_[2], vsr_[2];   // this lane's loaded row scales (see soff)
+  auto issue = [&](int bs, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    // Resources end at key hi; past the range (bs >= hi) they are empty and
+    // every load reads zeros without a memory access.
+    const uint32_t rows_left = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(hi - bs, STEP)));
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Kb + (size_t)bs * ROWB), 0, rows_left * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Vb + (size_t)bs * ROWB), 0, rows_left * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.kscale + row0 + bs), 0, rows_left * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.vscale + row0 + bs), 0, rows_left * 4, 0x00020000);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        kc[BUF][hb][i] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 16 * hb * ROWB + 64 * i, 0, kNT);
+    ksr_[BUF] = __builtin_amdgcn_raw_buffer_load_b32(ksr, soff, 0, kNT);
+    vsr_[BUF] = __builtin_amdgcn_raw_buffer_load_b32(vsr, soff, 0, kNT);
+    // V rows into LDS buffer BUF of this wavefront (that buffer's previous
+    // transposing reads have all completed: each was waited for before its
+    // product).
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int n = 0; n < NCOPY; ++n)
+      copy16_buf_to_lds(vrs, vbuf + BUF * kMB * ROWB + 1024 * n, vsrc[n], 0);
+  };
+  constexpr int NVM = 4 + 2 + NCOPY;   // vector-memory operations per block
+
+  auto compute = [&](int bs, auto buf_c) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(buf_c)::value;
+    // The block's loads have landed once at most the next block's are
+    // outstanding.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<NVM>());
+
+    // S' = K Q^T per half-block: lane holds keys 16*hb + 4*grp + r, head col.
+    f32x4 sacc[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 a = e4m3x8_to_bf16(kc[BUF][hb][kk >> 1][2 * (kk & 1)], kc[BUF][hb][kk >> 1][2 * (kk & 1) + 1]);
+        bf16x8 ab;
+        __builtin_memcpy(&ab, &a, sizeof(ab));
+        sacc[hb] = mma_16x16x32(ab, qb[kk], sacc[hb]);
+      }
+    }
+
+    // Row scales of the lane's keys kappa(grp, j): lane j of its row holds
+    // them (DPP row_newbcast:j).
+    float ksv[8], vsv[8];
+    static_for<0, 8>([&](auto j_c) {
+      constexpr int J = decltype(j_c)::value;
+      ksv[J] = __uint_as_float(__builtin_amdgcn_update_dpp(0u, ksr_[BUF], 0x150 + J, 0xf, 0xf, false));
+      vsv[J] = __uint_as_float(__builtin_amdgcn_update_dpp(0u, vsr_[BUF], 0x150 + J, 0xf, 0xf, false));
+    });
+
+    // Online softmax over the block (raw score units; K row scale applied).
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sc[j] = sacc[j >> 2][j & 3] * ksv[j];
+    if (bs + STEP > hi) {   // last block: keys past the range get -inf
+      const int k0 = bs + kMB * wave + 4 * grp;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + 16 * (j >> 2) + (j & 3) >= hi) sc[j] = kNegInf;
+    }
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+    mt = fmaxf(fmaxf(mt, sc[3]), sc[4]);
+    mt = fmaxf(fmaxf(mt, sc[5]), sc[6]);
+    mt = groups_max(fmaxf(mt, sc[7]));
+    const float m_new = fmaxf(m_run, mt);
+    const float mref = m_new == kNegInf ? 0.f : m_new;
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float corr = exp2_fast((m_run - mref) * c);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= corr;
+    }
+    m_run = m_new;
+    const float mc = mref * c;
+    float pe[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      pe[j] = exp2_fast(fmaf(sc[j], c, -mc));
+      l_run += pe[j];
+      pe[j] *= vsv[j];   // V row scale, after the row sum
+    }
+    bf16x8 pb;
+    {
+      const u32x4 w = {bf16_pair_bits(pe[0], pe[1]), bf16_pair_bits(pe[2], pe[3]),
+                       bf16_pair_bits(pe[4], pe[5]), bf16_pair_bits(pe[6], pe[7])};
+      __builtin_memcpy(&pb, &w, sizeof(pb));
+    }
+
+    // O^T += V^T P^T with V^T from LDS buffer BUF.
+    constexpr int VOFF = BUF * kMB * ROWB;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x2 t = lds_read_tr8<VOFF>(vaddr[db]);
+      lgkm_wait<0>();
+      tie(t);
+      const u32x4 w = e4m3x8_to_bf16(t[0], t[1]);
+      bf16x8 va;
+      __builtin_memcpy(&va, &w, sizeof(va));
+      oacc[db] = mma_16x16x32(va, pb, oacc[db]);
+    }
+  };
+
+  // The next block is always issued (an empty one past the range), so that
+  // every path through the loop has the same loads in flight.
+  if (lo < hi) {
+    issue(lo, IC<0>{});
+    for (int bs = lo;; bs += 2 * STEP) {
+      issue(bs + STEP, IC<1>{});
+      compute(bs, IC<0>{});
+      if (bs + STEP >= hi) break;
+      issue(bs + 2 * STEP, IC<0>{});
+      compute(bs + STEP, IC<1>{});
+      if (bs + 2 * STEP >= hi) break;
+    }
+    // No copy into LDS may still be in flight once the loop is left.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+  }
+
+  // Wavefront result per head: l summed over the lane groups, O^T element
+  // (16*db + 4*grp + r, col) in register r of block db.
+  const float lt = groups_sum(l_run);
+  if (col < HPW) {
+    if (grp == 0) {
+      red_m[wave][col] = m_run;
+      red_l[wave][col] = lt;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_o[wave][col][16 * db + 4 * grp + r] = oacc[db][r];
+  }
+  __syncthreads();
+
+  // Merge the 4 wavefronts (fixed order) and write the partial.
+  for (int i = tid; i < HPW * D; i += kDecThreads) {
+    const int h = i / D;
+    const int d = i % D;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, red_m[w][h]);
+    const float Mref = M == kNegInf ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = exp2_fast((red_m[w][h] - Mref) * c);
+      L = fmaf(wt, red_l[w][h], L);
+      O = fmaf(wt, red_o[w][h][d], O);
+    }
+    const size_t pi = slot * HPW + h;
+    p.part_o[pi * D + d] = O;
+    if (d == 0) {
+      p.part_m[pi] = M * c;   // stored in base-2 exponent units
+      p.part_l[pi] = L;
+    }
+  }
+  __syncthreads();   // LDS is reused by the next range
+}
+
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return min(max(p.seqlens[b], 0), p.Tk_max);
 }
@@ -391,6 +719,8 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams 
   __shared__ float red_m[4][HPW];
   __shared__ float red_l[4][HPW];
   __shared__ float red_o[4][HPW][D];
+  constexpr bool MF = FP8 && D == 128 && HPW >= 4;   // matrix-core range loop
+  __shared__ __attribute__((aligned(16))) uint8_t vlds[MF ? 2 * 4 * kMB * kMfRowB : 16];
   __shared__ long long wave_tot[4];
   __shared__ int start[3];
 
@@ -464,8 +794,12 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams 
     const int cnt = (int)min((long long)(n - key), pend - pos);
     const int kvh = j / groups;
     const int hq0 = kvh * p.g + (j % groups) * HPW;
-    decode_range_keys<D, HPW, KU, FP8>(p, b, kvh, hq0, key, key + cnt,
-                                       (size_t)w + (size_t)b * G + j, red_m, red_l, red_o);
+    if constexpr (MF)
+      decode_range_mfma<HPW>(p, b, kvh, hq0, key, key + cnt, (size_t)w + (size_t)b * G + j,
+                                  red_m, red_l, red_o, vlds);
+    else
+      decode_range_keys<D, HPW, KU, FP8>(p, b, kvh, hq0, key, key + cnt,
+                                         (size_t)w + (size_t)b * G + j, red_m, red_l, red_o);
     pos += cnt;
     if (pos >= pend) break;
     key = 0;

@@ -48,6 +48,7 @@ SMALL = [
     (2, 8, 1, 513, 64, [513, 300]),                    # g = 8
     (2, 2, 2, 96, 128, [96, 40]),                      # g = 1
     (2, 16, 2, 333, 128, [333, 17]),                   # g = 8, d = 128
+    (4, 8, 2, 300, 128, [0, 5, 33, 300]),              # empty and short, d = 128
 ]
 
 
