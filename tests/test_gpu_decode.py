@@ -42,6 +42,8 @@ SMALL = [
     (5, 6, 2, 257, 128, [257, 1, 128, 127, 200]),      # g = 3
     (2, 8, 1, 513, 64, [513, 300]),                    # g = 8
     (2, 2, 2, 96, 128, [96, 40]),                      # g = 1
+    (2, 16, 1, 150, 128, [150, 77]),                   # g = 16: two head groups per kv head
+    (2, 12, 1, 90, 64, [90, 1]),                       # g = 12: three groups of 4
 ]
 
 

@@ -49,6 +49,8 @@ SMALL = [
     (2, 2, 2, 96, 128, [96, 40]),                      # g = 1
     (2, 16, 2, 333, 128, [333, 17]),                   # g = 8, d = 128
     (4, 8, 2, 300, 128, [0, 5, 33, 300]),              # empty and short, d = 128
+    (2, 32, 2, 150, 128, [150, 77]),                   # g = 16: two head groups per kv head
+    (2, 12, 1, 140, 128, [140, 3]),                    # g = 12: three groups of 4
 ]
 
 
