@@ -132,7 +132,7 @@ class Decode:
     seq_lo: int
     seq_hi: int
     seed: int = 0
-    kv_dtype: str = "bf16"       # "bf16", or "fp8": E4M3 codes with one fp32 scale per row
+    kv_dtype: str = "bf16"       # "bf16"; "fp8" (E4M3) or "int8" codes with one fp32 scale per row
 
     @property
     def scale(self) -> float:
@@ -171,6 +171,10 @@ FLASH_DECODE_FP8 = Decode("split-KV decode over an fp8 (E4M3, per-row scale) cac
                           "Hkv=8, d=128, seqlen U[1024,32768]",
                           B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768,
                           kv_dtype="fp8")
+FLASH_DECODE_INT8 = Decode("split-KV decode over an int8 (per-row scale) cache, B=16, Hq=32, "
+                           "Hkv=8, d=128, seqlen U[1024,32768]",
+                           B=16, Hq=32, Hkv=8, Tk_max=32768, d=128, seq_lo=1024, seq_hi=32768,
+                           kv_dtype="int8")
 
 WORKLOADS = {
     "single_head_f32": SINGLE_HEAD_F32,
@@ -183,6 +187,7 @@ WORKLOADS = {
     "llama3_8b_long_fp8": LLAMA3_8B_LONG_FP8,
     "flash_decode": FLASH_DECODE,
     "flash_decode_fp8": FLASH_DECODE_FP8,
+    "flash_decode_int8": FLASH_DECODE_INT8,
 }
 
 
@@ -278,6 +283,43 @@ def decode_inputs_fp8(w: Decode, *, seed: Optional[int] = None, poison_tail: boo
         for b, n in enumerate(seqlens):
             kc[b, :, n:, :] = 0x7F
             vc[b, :, n:, :] = 0x7F
+    return q, kc, vc, ks, vs, seqlens
+
+
+INT8_MAX = 127   # largest code magnitude the int8 quantiser writes
+
+
+def quantize_rows_int8(x: np.ndarray):
+    """Per-row symmetric scaling of fp32 rows (last axis) to int8 codes, as a
+    cache writer would store them: scale = max|row| / 127 (1 for an all-zero
+    row), codes = round-half-to-even of row / scale, in [-127, 127], stored as
+    their two's-complement bytes.  Returns (codes uint8, scales float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(INT8_MAX), np.float32(1.0)).astype(np.float32)
+    y = np.rint(x / scale[..., None])
+    codes = np.clip(y, -INT8_MAX, INT8_MAX).astype(np.int8)
+    return codes.view(np.uint8), scale
+
+
+def decode_inputs_int8(w: Decode, *, seed: Optional[int] = None, poison_tail: bool = False):
+    """Return (q, kcodes, vcodes, kscale, vscale, seqlens) for an int8-cache
+    decode, drawn exactly as ``decode_inputs_fp8`` draws them and stored with
+    ``quantize_rows_int8``.  With ``poison_tail`` every slot at or beyond
+    seqlens[b] holds the code -128 (which the quantiser never writes)."""
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    seqlens = rng.integers(w.seq_lo, w.seq_hi, w.B, endpoint=True).astype(np.int32)
+    q = _draw(rng, (w.B, w.Hq, w.d), "bf16")
+    k = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "f32")
+    v = _draw(rng, (w.B, w.Hkv, w.Tk_max, w.d), "f32")
+    kc, ks = quantize_rows_int8(k)
+    del k
+    vc, vs = quantize_rows_int8(v)
+    del v
+    if poison_tail:
+        for b, n in enumerate(seqlens):
+            kc[b, :, n:, :] = 0x80
+            vc[b, :, n:, :] = 0x80
     return q, kc, vc, ks, vs, seqlens
 
 

@@ -24,7 +24,9 @@ from .attention import (  # noqa: F401
     attention_backward,
     decode_attention,
     decode_attention_fp8,
+    decode_attention_int8,
     e4m3_to_f64,
+    int8_to_f64,
     fp8_attention_inputs,
     decode_split_merge,
     online_normalizer,

@@ -403,6 +403,40 @@ def decode_attention_fp8(q, kcodes, vcodes, kscale, vscale, seqlens) -> Tuple[np
     return O, L
 
 
+def int8_to_f64(codes) -> np.ndarray:
+    """Values of 8-bit two's-complement integer codes: code c stands for c
+    when its top bit is clear and for c - 256 when it is set (-128 .. 127)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def decode_attention_int8(q, kcodes, vcodes, kscale, vscale, seqlens) -> Tuple[np.ndarray, np.ndarray]:
+    """Decode over an int8 cache: dequantize, then the decode definition.
+
+    Same layout and meaning as ``decode_attention_fp8`` with two's-complement
+    integer codes: K[b,h,j,:] = kscale[b,h,j] * int8(kcodes[b,h,j,:]) (V
+    alike), the other common low-bit cache format with a per-row block scale
+    ([NOTE] section on fused dequantisation).  Rows at or past seqlens[b] are
+    never read.
+    """
+    B, Hq, d = q.shape
+    Hkv = kcodes.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / math.sqrt(d)
+    O = np.zeros((B, Hq, vcodes.shape[3]))
+    L = np.full((B, Hq), _NEG_INF)
+    for b in range(B):
+        n = int(seqlens[b])
+        for kh in range(Hkv):
+            K = int8_to_f64(kcodes[b, kh, :n]) * np.asarray(kscale[b, kh, :n], np.float64)[:, None]
+            V = int8_to_f64(vcodes[b, kh, :n]) * np.asarray(vscale[b, kh, :n], np.float64)[:, None]
+            for h in range(kh * g, (kh + 1) * g):
+                Qr = as_f64(q[b, h])[None, :]
+                o, lse = _rows_three_pass(Qr, K, V, scale, np.ones((1, n), bool))
+                O[b, h], L[b, h] = o[0], lse[0]
+    return O, L
+
+
 def decode_split_merge(q, kcache, vcache, seqlens, num_splits: int,
                        tile: int = 64) -> Tuple[np.ndarray, np.ndarray]:
     """Flash-decoding in fp64: split each sequence's keys, merge the partials.

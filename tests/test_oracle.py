@@ -726,6 +726,69 @@ def test_fp8_row_quantisation_uses_the_full_range():
     assert np.max(rel) <= 16 / 448   # half the E4M3 spacing (32) of the top binade, relative to amax
 
 
+# ---------------------------------------------------------------------------
+# Decode over an int8 (two's-complement codes, per-row scale) cache
+# ---------------------------------------------------------------------------
+
+def test_int8_decoder_matches_torch_all_codes():
+    """Library routine: torch's reinterpretation of the 256 bytes as int8."""
+    torch = pytest.importorskip("torch")
+    c = np.arange(256, dtype=np.uint8)
+    a = oracle.int8_to_f64(c)
+    b = torch.from_numpy(c).view(torch.int8).to(torch.float64).numpy()
+    assert np.array_equal(a, b)
+
+
+def test_int8_format_values():
+    """Values fixed by two's complement: 0, +1, the extremes, -1."""
+    v = oracle.int8_to_f64(np.array([0x00, 0x01, 0x7F, 0x80, 0x81, 0xFF], np.uint8))
+    assert list(v) == [0.0, 1.0, 127.0, -128.0, -127.0, -1.0]
+
+
+def _small_int8_decode(poison=False):
+    w = inputs.Decode("t", B=3, Hq=8, Hkv=2, Tk_max=70, d=16, seq_lo=0, seq_hi=70, seed=6,
+                      kv_dtype="int8")
+    return inputs.decode_inputs_int8(w, poison_tail=poison)
+
+
+def test_int8_decode_is_decode_of_the_dequantized_cache():
+    """Dequantised with torch's int8 view times the row scales, the cache
+    gives the same result through the plain decode definition."""
+    torch = pytest.importorskip("torch")
+    q, kc, vc, ks, vs, sl = _small_int8_decode()
+    O, L = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
+    K = torch.from_numpy(kc).view(torch.int8).to(torch.float64).numpy() * ks[..., None]
+    V = torch.from_numpy(vc).view(torch.int8).to(torch.float64).numpy() * vs[..., None]
+    Or, Lr = oracle.decode_attention(q, K, V, sl)
+    assert np.array_equal(np.isinf(L), np.isinf(Lr))
+    assert np.max(np.abs(O - Or)) < 1e-14
+    fin = np.isfinite(Lr)
+    assert np.max(np.abs(L[fin] - Lr[fin])) < 1e-14
+
+
+def test_int8_decode_ignores_cache_beyond_seqlen():
+    q, kc, vc, ks, vs, sl = _small_int8_decode(poison=False)
+    O, L = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
+    q2, kc2, vc2, ks2, vs2, sl2 = _small_int8_decode(poison=True)
+    assert np.any(kc2 != kc)
+    O2, L2 = oracle.decode_attention_int8(q2, kc2, vc2, ks2, vs2, sl2)
+    assert np.array_equal(O, O2) and np.array_equal(L, L2)
+
+
+def test_int8_row_quantisation_uses_the_full_range():
+    """Input side: every stored row's largest code is +-127 (amax scaling),
+    no code is -128, and scale * code is within half a step of the drawn
+    value."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((5, 7, 32)).astype(np.float32)
+    codes, sc = inputs.quantize_rows_int8(x)
+    vals = oracle.int8_to_f64(codes)
+    assert np.all(np.max(np.abs(vals), axis=-1) == 127.0)
+    assert not np.any(codes == 0x80)
+    err = np.abs(vals * sc[..., None] - x) / sc[..., None]
+    assert np.max(err) <= 0.5 + 1e-5
+
+
 def test_fp8_attention_inputs_dequantise_with_torch():
     """Library routine: torch's E4M3 widening times the block scales (per
     query row; per batch and kv head for k and v)."""
