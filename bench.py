@@ -196,19 +196,25 @@ def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
     sl = torch.from_numpy(seqlens).cuda()
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-    if w.kv_dtype == "fp8":
-        # E4M3 codes of N(0,1)/max scaled rows: the byte pattern of a
+    if w.kv_dtype in ("fp8", "int8"):
+        # Codes of N(0,1) rows scaled to the code range (E4M3 by torch's
+        # conversion, int8 by rounding and clamping): the byte pattern of a
         # quantised cache; uniform random scales of the same order.
-        fp8 = []
+        coded = []
         for kc, vc in caches:
             ks = torch.rand((w.B, w.Hkv, w.Tk_max), generator=gen, device="cuda") * 0.01 + 0.005
             vs = torch.rand((w.B, w.Hkv, w.Tk_max), generator=gen, device="cuda") * 0.01 + 0.005
-            k8 = (kc * 40).to(torch.float8_e4m3fn).view(torch.uint8)
-            v8 = (vc * 40).to(torch.float8_e4m3fn).view(torch.uint8)
-            fp8.append((k8, v8, ks, vs))
+            if w.kv_dtype == "fp8":
+                k8 = (kc * 40).to(torch.float8_e4m3fn).view(torch.uint8)
+                v8 = (vc * 40).to(torch.float8_e4m3fn).view(torch.uint8)
+            else:
+                k8 = (kc * 40).round().clamp(-127, 127).to(torch.int8).view(torch.uint8)
+                v8 = (vc * 40).round().clamp(-127, 127).to(torch.int8).view(torch.uint8)
+            coded.append((k8, v8, ks, vs))
         del caches
-        caches = fp8
-        calls = [fa.prepared("fa_decode_fp8", q, k8, v8, ks, vs, sl, o, w.B, w.Hq, w.Hkv,
+        caches = coded
+        entry = "fa_decode_fp8" if w.kv_dtype == "fp8" else "fa_decode_int8"
+        calls = [fa.prepared(entry, q, k8, v8, ks, vs, sl, o, w.B, w.Hq, w.Hkv,
                              w.Tk_max, w.d, num_splits, stream=stream)
                  for k8, v8, ks, vs in caches]
         row_bytes = w.d + 4   # codes plus the fp32 row scale, per tensor
@@ -428,23 +434,24 @@ def main():
                                              "frac": round(gbs / PEAK_HBM_GBS, 4),
                                              "traffic": measured_traffic("flash_decode")}}
         log(f"[bench]   {also['flash_decode']}")
-        w8 = inputs.FLASH_DECODE_FP8
-        S8 = fa.fa_decode_fp8_workgroups(w8.B, w8.Hq, w8.Hkv, w8.Tk_max, w8.d, args.decode_splits)
-        log(f"[bench] {w8.name}, {S8} key ranges")
-        wl8, ev8, nbytes8, ntok8 = decode_case(torch, fa, w8, 200, 100, args.decode_splits)
-        gbs8 = nbytes8 / (ev8 * 1e-3) / 1e9
-        also["flash_decode_fp8"] = {"value": round(nbytes8 / wl8 / 1e9, 1), "unit": "GB/s",
-                                    "read_probe_gbs": round(ceil_gbs, 1),
-                                    "frac_of_read_probe": round(gbs8 / ceil_gbs, 4),
-                                    "us_per_call": round(wl8 * 1e6, 2),
-                                    "call_us_events": round(ev8 * 1e3, 2), "num_splits": S8,
-                                    "algorithmic_bytes": nbytes8, "kv_tokens": ntok8,
-                                    "speedup_vs_bf16_cache": round(ev / ev8, 3),
-                                    "roofline": {"bound": "hbm", "achieved": round(gbs8, 1),
-                                                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                                 "frac": round(gbs8 / PEAK_HBM_GBS, 4),
-                                                 "traffic": measured_traffic("flash_decode_fp8")}}
-        log(f"[bench]   {also['flash_decode_fp8']}")
+        for key, w8, plan in (("flash_decode_fp8", inputs.FLASH_DECODE_FP8, fa.fa_decode_fp8_workgroups),
+                              ("flash_decode_int8", inputs.FLASH_DECODE_INT8, fa.fa_decode_int8_workgroups)):
+            S8 = plan(w8.B, w8.Hq, w8.Hkv, w8.Tk_max, w8.d, args.decode_splits)
+            log(f"[bench] {w8.name}, {S8} key ranges")
+            wl8, ev8, nbytes8, ntok8 = decode_case(torch, fa, w8, 200, 100, args.decode_splits)
+            gbs8 = nbytes8 / (ev8 * 1e-3) / 1e9
+            also[key] = {"value": round(nbytes8 / wl8 / 1e9, 1), "unit": "GB/s",
+                         "read_probe_gbs": round(ceil_gbs, 1),
+                         "frac_of_read_probe": round(gbs8 / ceil_gbs, 4),
+                         "us_per_call": round(wl8 * 1e6, 2),
+                         "call_us_events": round(ev8 * 1e3, 2), "num_splits": S8,
+                         "algorithmic_bytes": nbytes8, "kv_tokens": ntok8,
+                         "speedup_vs_bf16_cache": round(ev / ev8, 3),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs8, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs8 / PEAK_HBM_GBS, 4),
+                                      "traffic": measured_traffic(key)}}
+            log(f"[bench]   {also[key]}")
         result["also"] = also
 
     if not args.no_cpu_baseline:

@@ -109,17 +109,17 @@ constexpr int kMaxDecodeWorkgroups = 1 << 20;
 // and all of them finish together.  Cached per (device, d, heads per
 // workgroup, cache type).  Returns a negative status if the device cannot be
 // queried.
-int decode_workgroups(int d, int hpw, bool fp8, int num_splits) {
+int decode_workgroups(int d, int hpw, int kv, int num_splits) {
   if (num_splits > 0) return num_splits < kMaxDecodeWorkgroups ? num_splits : kMaxDecodeWorkgroups;
   static std::mutex mu;
   static std::map<std::pair<int, int>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -FA_ERR_DEVICE;
-  const std::pair<int, int> key(dev, (d * 16 + hpw) * 2 + (fp8 ? 1 : 0));
+  const std::pair<int, int> key(dev, (d * 16 + hpw) * 4 + kv);
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  const int w = fa::decode_resident_workgroups(d, hpw, fp8);
+  const int w = fa::decode_resident_workgroups(d, hpw, kv);
   if (w <= 0) return -FA_ERR_DEVICE;
   cache[key] = w;
   return w;
@@ -232,29 +232,30 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
 namespace {
 
-int decode_workgroups_checked(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, bool fp8) {
+int decode_workgroups_checked(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, int kv) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0 || Hq % Hkv != 0)
     return -FA_ERR_SHAPE;
   if (d != 64 && d != 128) return -FA_ERR_UNSUPPORTED;
-  return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), fp8, num_splits);
+  return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), kv, num_splits);
 }
 
 int decode_impl(const void* q, const void* kcache, const void* vcache, const float* kscale,
                 const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
-                int Tk_max, int d, int num_splits, bool fp8, void* stream) {
+                int Tk_max, int d, int num_splits, int kv, void* stream) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Hq == 0) return FA_OK;
   if (q == nullptr || o == nullptr || seqlens == nullptr) return FA_ERR_NULL;
   if (Tk_max > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_NULL;
-  if (fp8 && Tk_max > 0 && (kscale == nullptr || vscale == nullptr)) return FA_ERR_NULL;
+  const bool codes = kv != fa::kKvBf16;
+  if (codes && Tk_max > 0 && (kscale == nullptr || vscale == nullptr)) return FA_ERR_NULL;
   // One merge wavefront per (sequence, query head).
   if ((int64_t)B * Hq > INT32_MAX / 2) return FA_ERR_SHAPE;
 
   const int g = Hq / Hkv;
   const int hpw = fa::decode_heads_per_workgroup(g);
-  const int W = decode_workgroups(d, hpw, fp8, num_splits);
+  const int W = decode_workgroups(d, hpw, kv, num_splits);
   if (W < 0) return -W;
   const size_t slots = fa::decode_slots(W, B, Hkv, g, hpw);
   const size_t cum_bytes = (((size_t)B + 1) * sizeof(long long) + 255) / 256 * 256;
@@ -270,8 +271,8 @@ int decode_impl(const void* q, const void* kcache, const void* vcache, const flo
   p.q = q;
   p.kcache = kcache;
   p.vcache = vcache;
-  p.kscale = fp8 ? kscale : nullptr;
-  p.vscale = fp8 ? vscale : nullptr;
+  p.kscale = codes ? kscale : nullptr;
+  p.vscale = codes ? vscale : nullptr;
   p.seqlens = seqlens;
   p.o = o;
   p.cum = (long long*)ws;
@@ -286,30 +287,41 @@ int decode_impl(const void* q, const void* kcache, const void* vcache, const flo
   p.hpw = hpw;
   p.W = W;
   p.c = (float)(1.4426950408889634 / sqrt((double)d));
-  return map_err(fa::launch_decode(p, d, fp8, hs));
+  return map_err(fa::launch_decode(p, d, kv, hs));
 }
 
 }  // namespace
 
 int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
-  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, false);
+  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, fa::kKvBf16);
 }
 
 int fa_decode_fp8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
-  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, true);
+  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, fa::kKvE4m3);
+}
+
+int fa_decode_int8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
+  return decode_workgroups_checked(B, Hq, Hkv, Tk_max, d, num_splits, fa::kKvInt8);
 }
 
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens, void* o,
               int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, void* stream) {
   return decode_impl(q, kcache, vcache, nullptr, nullptr, seqlens, o, B, Hq, Hkv, Tk_max, d,
-                     num_splits, false, stream);
+                     num_splits, fa::kKvBf16, stream);
 }
 
 int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* kscale,
                   const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
                   int Tk_max, int d, int num_splits, void* stream) {
   return decode_impl(q, kcache, vcache, kscale, vscale, seqlens, o, B, Hq, Hkv, Tk_max, d,
-                     num_splits, true, stream);
+                     num_splits, fa::kKvE4m3, stream);
+}
+
+int fa_decode_int8(const void* q, const void* kcache, const void* vcache, const float* kscale,
+                   const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
+                   int Tk_max, int d, int num_splits, void* stream) {
+  return decode_impl(q, kcache, vcache, kscale, vscale, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                     num_splits, fa::kKvInt8, stream);
 }
 
 int fa_read_probe(const void* src, size_t bytes, unsigned* sink, void* stream) {

@@ -142,6 +142,40 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// Int8 code k (byte k, two's complement) of a word as a float.
+__device__ __forceinline__ float int8_at(uint32_t w, int k) {
+  return (float)((int32_t)(w << (24 - 8 * k)) >> 24);
+}
+// Widen 8 int8 codes (two words) to one 16-byte vector of bf16 pairs, in
+// order; exact (every integer in [-128, 127] is a bf16 value).
+__device__ __forceinline__ u32x4 int8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return u32x4{bf16_pair_bits(int8_at(w0, 0), int8_at(w0, 1)), bf16_pair_bits(int8_at(w0, 2), int8_at(w0, 3)),
+               bf16_pair_bits(int8_at(w1, 0), int8_at(w1, 1)), bf16_pair_bits(int8_at(w1, 2), int8_at(w1, 3))};
+}
+// 8 codes (two words) of an 8-bit cache of kind KV as 8 bf16 values, in order.
+template <int KV>
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  if constexpr (KV == kKvInt8) return int8x8_to_bf16(w0, w1);
+  else return e4m3x8_to_bf16(w0, w1);
+}
+// Codes k = 0..3 of the words wa and wb (two keys) as (v_a, v_b) bf16 pairs.
+// E4M3: byte-interleave first (a0 b0 a1 b1, a2 b2 a3 b3), so that each
+// widening gives one pair directly.
+template <int KV>
+__device__ __forceinline__ void pairs4(uint32_t wa, uint32_t wb, bf16x2 (&v2)[4]) {
+  if constexpr (KV == kKvInt8) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v2[k] = to_bf16x2(int8_at(wa, k), int8_at(wb, k));
+  } else {
+    const uint32_t x0 = __builtin_amdgcn_perm(wb, wa, 0x05010400u);
+    const uint32_t x1 = __builtin_amdgcn_perm(wb, wa, 0x07030602u);
+    v2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false);
+    v2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true);
+    v2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false);
+    v2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true);
+  }
+}
+
 // Attention of the HPW query heads hq0.. over keys [lo, hi) of kv head
 // (b, kvh); the partial (m, l, o) goes to `slot`.  Every thread of the
 // workgroup calls this with the same arguments.  FP8: the cache holds E4M3
@@ -149,12 +183,13 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // load, widens them to bf16 in registers and the rest of the loop is the
 // bf16 one, with the K row scale applied to the row's score and the V row
 // scale to its probability (after the row sum l is formed).
-template <int D, int HPW, int KU, bool FP8>
+template <int D, int HPW, int KU, int KV>
 __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, int kvh, int hq0,
                                                   int lo, int hi, size_t slot, float (*red_m)[HPW],
                                                   float (*red_l)[HPW], float (*red_o)[HPW][D]) {
   typedef DecodeShape<D, HPW> S;
   constexpr int EPL = S::EPL, LPR = S::LPR, RPW = S::RPW, NV = S::NV;
+  constexpr bool FP8 = KV != kKvBf16;   // an 8-bit cache (E4M3 or int8 codes)
   constexpr int STEP = 4 * RPW * KU;   // keys per workgroup iteration
   static_assert(KU % 2 == 0, "keys are paired within a lane");
   // The range is the same for the whole workgroup; keep it in scalar
@@ -263,7 +298,7 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
       float acc[HPW];
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
-        const u32x4 k4 = FP8 ? e4m3x8_to_bf16(kb[u][2 * j], kb[u][2 * j + 1]) : kr[u][j];
+        const u32x4 k4 = FP8 ? widen8<KV>(kb[u][2 * j], kb[u][2 * j + 1]) : kr[u][j];
 #pragma unroll
         for (int h = 0; h < HPW; ++h) {
           if (j == 0) acc[h] = dot2_from_zero(as_bf16x2(k4[0]), as_bf16x2(qv[h][0][0]));
@@ -329,13 +364,8 @@ __device__ __forceinline__ void decode_range_keys(const DecodeParams& p, int b, 
       for (int t = 0; t < KU / 2; ++t)
 #pragma unroll
         for (int i = 0; i < EPL / 4; ++i) {
-          const uint32_t wa = vb[2 * t][i], wb = vb[2 * t + 1][i];
-          const uint32_t x0 = __builtin_amdgcn_perm(wb, wa, 0x05010400u);
-          const uint32_t x1 = __builtin_amdgcn_perm(wb, wa, 0x07030602u);
-          const bf16x2 v2[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, false),
-                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x0, 1.0f, true),
-                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, false),
-                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x1, 1.0f, true)};
+          bf16x2 v2[4];
+          pairs4<KV>(vb[2 * t][i], vb[2 * t + 1][i], v2);
 #pragma unroll
           for (int k = 0; k < 4; ++k)
 #pragma unroll
@@ -461,7 +491,7 @@ __device__ __forceinline__ float groups_sum(float x) {
 
 // Same contract as decode_range_keys for the E4M3 cache (d = 128, HPW of 4
 // or 8); `vlds` holds 2 * 4 * kMB rows (two blocks per wavefront).
-template <int HPW>
+template <int HPW, int KV>
 __device__ __forceinline__ void decode_range_mfma(const DecodeParams& p, int b, int kvh, int hq0,
                                                   int lo, int hi, size_t slot, float (*red_m)[HPW],
                                                   float (*red_l)[HPW], float (*red_o)[HPW][128],
@@ -585,7 +615,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeParams& p, int b, 
       sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 a = e4m3x8_to_bf16(kc[BUF][hb][kk >> 1][2 * (kk & 1)], kc[BUF][hb][kk >> 1][2 * (kk & 1) + 1]);
+        const u32x4 a = widen8<KV>(kc[BUF][hb][kk >> 1][2 * (kk & 1)], kc[BUF][hb][kk >> 1][2 * (kk & 1) + 1]);
         bf16x8 ab;
         __builtin_memcpy(&ab, &a, sizeof(ab));
         sacc[hb] = mma_16x16x32(ab, qb[kk], sacc[hb]);
@@ -646,7 +676,7 @@ __device__ __forceinline__ void decode_range_mfma(const DecodeParams& p, int b, 
       u32x2 t = lds_read_tr8<VOFF>(vaddr[db]);
       lgkm_wait<0>();
       tie(t);
-      const u32x4 w = e4m3x8_to_bf16(t[0], t[1]);
+      const u32x4 w = widen8<KV>(t[0], t[1]);
       bf16x8 va;
       __builtin_memcpy(&va, &w, sizeof(va));
       oacc[db] = mma_16x16x32(va, pb, oacc[db]);
@@ -714,12 +744,12 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
 }
 
 // Workgroup w of W: balanced share of the key space of all segments.
-template <int D, int HPW, int KU, bool FP8>
+template <int D, int HPW, int KU, int KV>
 __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams p) {
   __shared__ float red_m[4][HPW];
   __shared__ float red_l[4][HPW];
   __shared__ float red_o[4][HPW][D];
-  constexpr bool MF = FP8 && D == 128 && HPW >= 4;   // matrix-core range loop
+  constexpr bool MF = KV != kKvBf16 && D == 128 && HPW >= 4;   // matrix-core range loop
   __shared__ __attribute__((aligned(16))) uint8_t vlds[MF ? 2 * 4 * kMB * kMfRowB : 16];
   __shared__ long long wave_tot[4];
   __shared__ int start[3];
@@ -795,10 +825,10 @@ __global__ void __launch_bounds__(kDecThreads) decode_kernel(const DecodeParams 
     const int kvh = j / groups;
     const int hq0 = kvh * p.g + (j % groups) * HPW;
     if constexpr (MF)
-      decode_range_mfma<HPW>(p, b, kvh, hq0, key, key + cnt, (size_t)w + (size_t)b * G + j,
+      decode_range_mfma<HPW, KV>(p, b, kvh, hq0, key, key + cnt, (size_t)w + (size_t)b * G + j,
                                   red_m, red_l, red_o, vlds);
     else
-      decode_range_keys<D, HPW, KU, FP8>(p, b, kvh, hq0, key, key + cnt,
+      decode_range_keys<D, HPW, KU, KV>(p, b, kvh, hq0, key, key + cnt,
                                          (size_t)w + (size_t)b * G + j, red_m, red_l, red_o);
     pos += cnt;
     if (pos >= pend) break;
@@ -902,29 +932,34 @@ __global__ void __launch_bounds__(64) decode_merge_kernel(const DecodeParams p) 
   }
 }
 
-template <int D, int HPW, bool FP8>
+template <int D, int HPW, int KV>
 const void* decode_kernel_ptr() {
-  return (const void*)decode_kernel<D, HPW, kDecKU, FP8>;
+  return (const void*)decode_kernel<D, HPW, kDecKU, KV>;
 }
 
-template <int D, bool FP8>
+template <int D, int KV>
 const void* decode_kernel_for(int hpw) {
   switch (hpw) {
-    case 8: return decode_kernel_ptr<D, 8, FP8>();
-    case 4: return decode_kernel_ptr<D, 4, FP8>();
-    case 2: return decode_kernel_ptr<D, 2, FP8>();
-    default: return decode_kernel_ptr<D, 1, FP8>();
+    case 8: return decode_kernel_ptr<D, 8, KV>();
+    case 4: return decode_kernel_ptr<D, 4, KV>();
+    case 2: return decode_kernel_ptr<D, 2, KV>();
+    default: return decode_kernel_ptr<D, 1, KV>();
   }
 }
 
-template <int D, bool FP8>
+template <int KV>
+const void* decode_kernel_dk(int d, int hpw) {
+  return d == 64 ? decode_kernel_for<64, KV>(hpw) : decode_kernel_for<128, KV>(hpw);
+}
+
+template <int D, int KV>
 hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.W);
   switch (p.hpw) {
-    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
-    default: hipLaunchKernelGGL((decode_kernel<D, 1, kDecKU, FP8>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<D, 8, kDecKU, KV>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<D, 4, kDecKU, KV>), grid, dim3(kDecThreads), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<D, 2, kDecKU, KV>), grid, dim3(kDecThreads), 0, stream, p); break;
+    default: hipLaunchKernelGGL((decode_kernel<D, 1, kDecKU, KV>), grid, dim3(kDecThreads), 0, stream, p); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -932,19 +967,28 @@ hipError_t launch_decode_d(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
-  if (fp8) return d == 64 ? launch_decode_d<64, true>(p, stream) : launch_decode_d<128, true>(p, stream);
-  return d == 64 ? launch_decode_d<64, false>(p, stream) : launch_decode_d<128, false>(p, stream);
+template <int KV>
+hipError_t launch_decode_k(const DecodeParams& p, int d, hipStream_t stream) {
+  return d == 64 ? launch_decode_d<64, KV>(p, stream) : launch_decode_d<128, KV>(p, stream);
 }
 
-int decode_resident_workgroups(int d, int hpw, bool fp8) {
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int d, int kv, hipStream_t stream) {
+  switch (kv) {
+    case kKvE4m3: return launch_decode_k<kKvE4m3>(p, d, stream);
+    case kKvInt8: return launch_decode_k<kKvInt8>(p, d, stream);
+    default: return launch_decode_k<kKvBf16>(p, d, stream);
+  }
+}
+
+int decode_resident_workgroups(int d, int hpw, int kv) {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  const void* k = fp8 ? (d == 64 ? decode_kernel_for<64, true>(hpw) : decode_kernel_for<128, true>(hpw))
-                      : (d == 64 ? decode_kernel_for<64, false>(hpw) : decode_kernel_for<128, false>(hpw));
+  const void* k = kv == kKvE4m3   ? decode_kernel_dk<kKvE4m3>(d, hpw)
+                  : kv == kKvInt8 ? decode_kernel_dk<kKvInt8>(d, hpw)
+                                  : decode_kernel_dk<kKvBf16>(d, hpw);
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kDecThreads, 0) != hipSuccess) return 0;
   return cus * per_cu;
 }

@@ -34,9 +34,9 @@ struct FwdParams {
 // w + segment.  The merge kernel combines the slots of each segment.
 struct DecodeParams {
   const void* q;
-  const void* kcache;   // bf16, or E4M3 codes (one byte per element)
+  const void* kcache;   // bf16, or 8-bit codes (one byte per element)
   const void* vcache;
-  const float* kscale;  // E4M3 cache: one scale per row, [B, Hkv, Tk_max]; else null
+  const float* kscale;  // 8-bit cache: one scale per row, [B, Hkv, Tk_max]; else null
   const float* vscale;
   const int* seqlens;
   void* o;
@@ -85,10 +85,16 @@ hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t s
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
+// Element type of a decode KV cache.
+enum KvKind : int {
+  kKvBf16 = 0,   // bf16 elements
+  kKvE4m3 = 1,   // E4M3 codes with one fp32 scale per row
+  kKvInt8 = 2,   // two's-complement int8 codes with one fp32 scale per row
+};
+hipError_t launch_decode(const DecodeParams& p, int d, int kv, hipStream_t stream);
 // Workgroups that the decode kernel for (d, hpw, cache type) keeps resident
 // on the current device at once; 0 if the device cannot be queried.
-int decode_resident_workgroups(int d, int hpw, bool fp8);
+int decode_resident_workgroups(int d, int hpw, int kv);
 // Streams `bytes` (a multiple of 16) from src once, XOR-folding them into
 // *sink (which the caller zeroes).
 hipError_t launch_read_probe(const void* src, size_t bytes, unsigned* sink, hipStream_t stream);

@@ -1,7 +1,7 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
 The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
-``fa_decode_fp8``, ``fa_decode_fp8_workgroups``,
+``fa_decode_fp8``, ``fa_decode_fp8_workgroups``, ``fa_decode_int8``, ``fa_decode_int8_workgroups``,
 ``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
 with a ``data_ptr()`` method (torch tensors), streams as integers, None (the
@@ -65,6 +65,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_decode_fp8.restype = I
         lib.fa_decode_fp8_workgroups.argtypes = [I, I, I, I, I, I]
         lib.fa_decode_fp8_workgroups.restype = I
+        lib.fa_decode_int8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.fa_decode_int8.restype = I
+        lib.fa_decode_int8_workgroups.argtypes = [I, I, I, I, I, I]
+        lib.fa_decode_int8_workgroups.restype = I
         lib.fa_strerror.argtypes = [I]
         lib.fa_strerror.restype = ctypes.c_char_p
         lib.fa_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
@@ -163,6 +167,20 @@ def fa_decode_fp8_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
     n = load().fa_decode_fp8_workgroups(B, Hq, Hkv, Tk_max, d, int(num_splits))
     if n < 0:
         raise FAError(-n, "fa_decode_fp8_workgroups")
+    return n
+
+
+def fa_decode_int8(q, kcache, vcache, kscale, vscale, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                   num_splits, stream=None) -> None:
+    _check(load().fa_decode_int8(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(kscale), _ptr(vscale),
+                                 _ptr(seqlens), _ptr(o), B, Hq, Hkv, Tk_max, d, int(num_splits),
+                                 _stream(stream)), "fa_decode_int8")
+
+
+def fa_decode_int8_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:
+    n = load().fa_decode_int8_workgroups(B, Hq, Hkv, Tk_max, d, int(num_splits))
+    if n < 0:
+        raise FAError(-n, "fa_decode_int8_workgroups")
     return n
 
 
@@ -288,10 +306,29 @@ def decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, *, num_splits: int = 
                stream=None):
     """Single-query attention over an E4M3 KV cache: q [B,Hq,d] bf16, caches
     [B,Hkv,Tmax,d] uint8 codes, scales [B,Hkv,Tmax] fp32, seqlens [B] int32."""
+    return _decode_codes(fa_decode_fp8, q, kcache, vcache, kscale, vscale, seqlens, num_splits,
+                         out, stream)
+
+
+def decode_int8(q, kcache, vcache, kscale, vscale, seqlens, *, num_splits: int = 0, out=None,
+                stream=None):
+    """Single-query attention over an int8 KV cache: q [B,Hq,d] bf16, caches
+    [B,Hkv,Tmax,d] int8 codes (torch int8 or their bytes as uint8), scales
+    [B,Hkv,Tmax] fp32, seqlens [B] int32."""
+    import torch
+    if kcache.dtype == torch.int8:
+        kcache = kcache.view(torch.uint8)
+    if vcache.dtype == torch.int8:
+        vcache = vcache.view(torch.uint8)
+    return _decode_codes(fa_decode_int8, q, kcache, vcache, kscale, vscale, seqlens, num_splits,
+                         out, stream)
+
+
+def _decode_codes(entry, q, kcache, vcache, kscale, vscale, seqlens, num_splits, out, stream):
     import torch
     _require(q.dim() == 3 and kcache.dim() == 4 and vcache.shape == kcache.shape, "bad shapes")
     _require(q.dtype == torch.bfloat16 and kcache.dtype == vcache.dtype == torch.uint8,
-             "q must be bf16 and the caches uint8 E4M3 codes")
+             "q must be bf16 and the caches one-byte codes")
     _require(kscale.dtype == vscale.dtype == torch.float32 and
              tuple(kscale.shape) == tuple(vscale.shape) == tuple(kcache.shape[:3]),
              "scales must be fp32 [B,Hkv,Tmax]")
@@ -304,6 +341,5 @@ def decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, *, num_splits: int = 
         out = torch.empty_like(q)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fa_decode_fp8(q, kcache, vcache, kscale, vscale, seqlens, out, B, Hq, Hkv, Tmax, d, num_splits,
-                  stream)
+    entry(q, kcache, vcache, kscale, vscale, seqlens, out, B, Hq, Hkv, Tmax, d, num_splits, stream)
     return out

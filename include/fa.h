@@ -236,9 +236,11 @@ int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_spli
  * same contract as fa_decode (q and o bf16, seqlens on the device, scale
  * 1/sqrt(d), num_splits, workspace, determinism, errors; FA_ERR_NULL also for
  * a NULL scale array when Tk_max > 0).  Arithmetic: codes widen exactly to
- * bf16; q.k as packed bf16 dot products with fp32 sums, times the K row
- * scale; the probability times the V row scale is rounded to bf16 for the
- * p.v product; the row sums use the unscaled fp32 probabilities.
+ * bf16; q.k with fp32 sums (on the bf16 matrix core at d = 128 with a group
+ * of 4 or 8 query heads per kv head or a multiple of it, else as packed bf16
+ * dot products), times the K row scale; the probability times the V row
+ * scale is rounded to bf16 for the p.v product; the row sums use the
+ * unscaled fp32 probabilities.
  */
 int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* kscale,
                   const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
@@ -246,6 +248,26 @@ int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const f
 
 /* fa_decode_workgroups for fa_decode_fp8. */
 int fa_decode_fp8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
+
+/*
+ * fa_decode_int8 -- fa_decode_fp8 with an int8 cache: the other common
+ * low-bit KV format with one scale per cached row ([NOTE] section
+ * "Prefill i dekodowanie to różne problemy").
+ *
+ *   kcache, vcache : [B, Hkv, Tk_max, d] int8 codes (two's complement, stored
+ *                    as bytes)
+ *   kscale, vscale : [B, Hkv, Tk_max] fp32, one scale per cached row
+ * Row j of kv head h of sequence b stands for
+ *     K[b,h,j,:] = kscale[b,h,j] * int8(kcache[b,h,j,:])   (V alike);
+ * contract, errors and arithmetic as fa_decode_fp8 (every int8 value widens
+ * exactly to bf16).
+ */
+int fa_decode_int8(const void* q, const void* kcache, const void* vcache, const float* kscale,
+                   const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
+                   int Tk_max, int d, int num_splits, void* stream);
+
+/* fa_decode_workgroups for fa_decode_int8. */
+int fa_decode_int8_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits);
 
 /*
  * fa_read_probe -- measurement utility, not part of the attention path:

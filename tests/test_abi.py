@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode", "fa_strerror",
               "fa_release_workspace", "fa_decode_workgroups", "fa_read_probe", "fa_decode_fp8",
-              "fa_decode_fp8_workgroups"):
+              "fa_decode_fp8_workgroups", "fa_decode_int8", "fa_decode_int8_workgroups"):
         assert n in names
 
 
@@ -140,6 +140,28 @@ def test_decode_validation(lib, args, status):
 ])
 def test_decode_fp8_validation(lib, args, status):
     assert lib.fa_decode_fp8(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    # (q, kc, vc, ks, vs, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits)
+    ((FAKE,) * 7 + (2, 8, 2, 64, 32, 4), 3),
+    ((FAKE,) * 7 + (2, 8, 3, 64, 128, 4), 2),
+    ((FAKE,) * 7 + (2, 8, 2, 64, 128, -1), 2),
+    ((FAKE, FAKE, FAKE, P, FAKE, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # kscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, P, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # vscale NULL
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, P, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # seqlens NULL
+    ((FAKE, FAKE, P, FAKE, FAKE, FAKE, FAKE) + (2, 8, 2, 64, 128, 4), 1),   # vcache NULL
+    ((P,) * 7 + (0, 8, 2, 64, 128, 4), 0),                                  # empty batch
+    ((FAKE,) * 7 + (1 << 28, 8, 2, 64, 128, 4), 2),
+])
+def test_decode_int8_validation(lib, args, status):
+    assert lib.fa_decode_int8(*args, None) == status
+
+
+def test_decode_int8_workgroup_planning(lib):
+    assert lib.fa_decode_int8_workgroups(16, 32, 8, 32768, 128, 16) == 16
+    assert lib.fa_decode_int8_workgroups(16, 30, 8, 32768, 128, 16) == -fa.STATUS_CODES["FA_ERR_SHAPE"]
+    assert lib.fa_decode_int8_workgroups(16, 32, 8, 32768, 96, 16) == -fa.STATUS_CODES["FA_ERR_UNSUPPORTED"]
 
 
 def test_decode_workgroup_planning(lib):
