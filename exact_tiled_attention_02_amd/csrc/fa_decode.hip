@@ -15,16 +15,17 @@
 //           reproducible).
 //
 // This work is bound by HBM bandwidth (about 4 FLOP per cache byte with a
-// group of 4; 8 with an 8-bit cache), so it runs on the vector ALUs; the design goal is to stream
-// every cache byte exactly once with coalesced 16-byte loads and enough
-// loads in flight, while spending as few vector instructions per key as
-// possible so that the arithmetic hides under the memory time.
+// group of 4; 8 with an 8-bit cache): the design goal is to stream every
+// cache byte exactly once with coalesced loads and enough of them in
+// flight, while spending as few vector instructions per key as possible so
+// that the arithmetic hides under the memory time.
 //
-// One workgroup per (piece s, kv head group, sequence b); pieces have the
-// same size for every sequence (the cache capacity divided by the split
-// count, rounded up to 64 keys), so workgroups carry equal work whatever the
-// sequence lengths:
-//  * 4 wavefronts march through the piece's keys.  A key row is read by LPR
+// W workgroups (as many as the device keeps resident) each take an equal
+// contiguous range of the key space of all (sequence, kv head group)
+// segments laid end to end, so every workgroup carries the same number of
+// keys whatever the sequence lengths; a range that crosses segments emits
+// one partial per segment it touches.  Within a range (packed-dot loop):
+//  * 4 wavefronts march through the range's keys.  A key row is read by LPR
 //    lanes (8 at d = 128 with up to 4 heads per workgroup, else 16 at
 //    d = 128 and 8 at d = 64), each lane holding EPL = d / LPR elements, so
 //    one load step of a wavefront covers 64 / LPR consecutive keys and every
@@ -42,14 +43,14 @@
 //    p_a v_a + p_b v_b to an fp32 accumulator.  The row sum l is formed from
 //    the unrounded fp32 probabilities.
 //  * At the end the rows of a wavefront are merged with the rescale rule
-//    (lane shuffles), then the 4 wavefronts through LDS, and the piece's
-//    (m, l, o) is written to the workspace.
-// An 8-bit cache (E4M3 codes, one fp32 scale per row: [NOTE]'s fused
+//    (lane shuffles), then the 4 wavefronts through LDS, and the range's
+//    (m, l, o) for the segment is written to the workspace.
+// An 8-bit cache (E4M3 or int8 codes, one fp32 scale per row: [NOTE]'s fused
 // dequantisation, the cache expanded inside the tile load) widens the codes
-// to bf16 in registers right after the load.  At d = 128 with 4 or 8 heads
-// per workgroup it runs a matrix-core loop (decode_range_mfma): the scores
-// and P.V on the 16x16x32 bf16 matrix core, V^T through LDS; otherwise the
-// packed-dot loop above.
+// exactly to bf16 in registers right after the load.  At d = 128 with 4 or 8
+// heads per workgroup it runs a matrix-core loop (decode_range_mfma): the
+// scores and P.V on the 16x16x32 bf16 matrix core, V^T through LDS;
+// otherwise the packed-dot loop above.
 // Merge kernel, one wavefront per (sequence, query head): fixed-order pass
 // over the pieces, O = sum 2^(m_s - M) o_s / sum 2^(m_s - M) l_s.
 #include "fa_device.h"
