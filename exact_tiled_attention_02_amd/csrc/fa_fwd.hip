@@ -111,6 +111,22 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Lazy reference of the bf16 kernel: the accumulator is rescaled only when a
+// row's max has grown past its reference by more than this many powers of 2.
+constexpr float kLazyLog2 = 8.f;
+
+// x / bf16(x).  The accumulator holds bf16-rounded probabilities times V
+// while l sums them unrounded, so a row dominated by one key would come out
+// scaled by that key's rounding ratio.  Against an exact running max the
+// largest probability is exactly 1 and has no rounding; against a lazy
+// reference it is 2^(m*c + nmc) in [1, 2^kLazyLog2], computed by the same
+// expression as in the tile, and multiplying the accumulator by this
+// ratio (at each move of the reference and at the end) undoes its rounding.
+__device__ __forceinline__ float top_fix(float x) {
+  const float r = (float)to_bf16x2(x, x)[0];
+  return x / r;
+}
+
 // ---------------------------------------------------------------------------
 // bf16 forward kernel
 // ---------------------------------------------------------------------------
@@ -270,7 +286,15 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   }
 
   const float c = p.c;
+  // Probabilities are taken against a reference max that moves only when
+  // some row's max exceeds its reference by more than 2^kLazyLog2 in
+  // probability (see the update below).  nmc = -reference * c, and thr is
+  // the raw score past which the reference must move.  A row with no key
+  // at all keeps nmc = 0; +inf makes the first rescale factor exactly 0.
+  const float lazy_raw = kLazyLog2 / c;
   float m = kNegInf;   // running max of this row's raw scores
+  float nmc = has_keys ? __builtin_inff() : 0.f;
+  float thr = kNegInf;
   float l = 0.f;       // this half-wave's share of the running sum
   f32x16 acc[ND];
 #pragma unroll
@@ -336,25 +360,34 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
     mt = max_halves(mt);
 
-    // Online update of the running max.  The accumulator is rescaled only
-    // when the max of some row of the wavefront actually grew ([FUSED07]
-    // "FlashAttention-2": rescale only if the maximum increased); l always
-    // takes its factor (exactly 1 where the max did not move).
-    const float m_new = fmaxf(m, mt);
-    const float corr = has_keys ? exp2_fast((m - m_new) * c) : 1.f;
-    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+    // Online update.  The running max m is exact; the reference the
+    // probabilities are taken against moves to it only when some row of the
+    // wavefront has outgrown its reference by more than 2^kLazyLog2
+    // ([FUSED07] "FlashAttention-2": rescale only when the maximum has
+    // increased; here only when it has increased by that much).  Between
+    // moves a probability may exceed 1 (by at most 2^kLazyLog2), which fp32
+    // and bf16 represent with the same relative precision.
+    const float m_prev = m;
+    m = fmaxf(m, mt);
+    if (__builtin_amdgcn_ballot_w64(m > thr) != 0) {
+      const float nmc_new = has_keys ? -m * c : 0.f;
+      const float corr = has_keys ? exp2_fast(nmc_new - nmc) : 1.f;
+      // The bf16 rounding of the largest probability so far, undone: see
+      // top_fix.  Rows without a previous key take 1.
+      const float fold = m_prev > kNegInf ? top_fix(exp2_fast(fmaf(m_prev, c, nmc))) : 1.f;
+      const float f = corr * fold;
 #pragma unroll
-      for (int i = 0; i < ND; ++i) acc[i] *= corr;
+      for (int i = 0; i < ND; ++i) acc[i] *= f;
+      l *= corr;
+      nmc = nmc_new;
+      thr = m + lazy_raw;
     }
-    l *= corr;
-    m = m_new;
-    const float mc = has_keys ? m * c : 0.f;
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[kb][r] = exp2_fast(fmaf(s[kb][r], c, -mc));
+        s[kb][r] = exp2_fast(fmaf(s[kb][r], c, nmc));
         ls[r & 3] += s[kb][r];
       }
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -417,9 +450,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     if (t + 3 < ntiles) tile(t + 3, IC<3>{});
   }
 
-  // Finalise: one division per row; lse in natural log.
+  // Finalise: one division per row, with the rounding of the row's largest
+  // probability undone (top_fix); lse in natural log.
   const float lt = sum_halves(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float fix = lt > 0.f ? top_fix(exp2_fast(fmaf(m, c, nmc))) : 1.f;
+  const float inv = lt > 0.f ? fix / lt : 0.f;
   if (active && my_q < p.Tq) {
     bf16* Og = (bf16*)p.o + ((size_t)(b * p.Hq + hq) * p.Tq + my_q) * D;
 #pragma unroll
@@ -432,7 +467,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       }
     if (p.lse != nullptr && half == 0)
       p.lse[(size_t)(b * p.Hq + hq) * p.Tq + my_q] =
-          lt > 0.f ? (m * c + __builtin_amdgcn_logf(lt)) * kLn2 : kNegInf;
+          lt > 0.f ? (__builtin_amdgcn_logf(lt) - nmc) * kLn2 : kNegInf;
   }
 }
 

@@ -233,6 +233,32 @@ def test_large_query_scale_stability():
     check("lse", L, Lr, max(BF16_LSE_TOL, 4e-6 * np.max(np.abs(Lr))))
 
 
+@pytest.mark.parametrize("d,growth", [(64, 3.0), (128, 3.0), (128, 12.0), (64, 0.4)])
+def test_slowly_growing_row_max(d, growth):
+    """Scores that rise along the key sequence, so every row's max grows tile
+    after tile by about `growth` powers of 2 per 64 keys.  The kernel moves
+    its reference max only when a row has outgrown it by more than 2^8, so
+    here most tiles run against a stale reference with probabilities above 1
+    (growth 3 and 0.4), or every tile moves it (growth 12); rows are peaked
+    on their last keys.  Output and lse must still match the oracle."""
+    rng = np.random.default_rng(11)
+    Tq = Tk = 1000
+    scale = 1.0 / math.sqrt(d)
+    c = scale * math.log2(math.e)
+    slope = growth / (64.0 * c)          # raw score increase per key
+    q = 0.5 * rng.standard_normal((1, 2, Tq, d)).astype(np.float32)
+    q[..., 0] += 1.0
+    k = rng.standard_normal((1, 1, Tk, d)).astype(np.float32)
+    k[..., 0] += slope * np.arange(Tk, dtype=np.float32)
+    v = rng.standard_normal((1, 1, Tk, d)).astype(np.float32)
+    q, k, v = (inputs.f32_to_bf16_bits(x) for x in (q, k, v))
+    say("fa_fwd bf16 rising scores d", d, "growth", growth)
+    O, L = run_bf16(q, k, v, True, scale)
+    Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=scale)
+    check("O", O, Or, BF16_O_TOL)
+    check("lse", L, Lr, BF16_LSE_TOL)
+
+
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
 def test_other_scales(scale):
     w = inputs.Prefill("t", B=1, Hq=2, Hkv=1, Tq=150, Tk=150, d=64, causal=True, seed=4)
