@@ -137,87 +137,89 @@ __device__ __forceinline__ float top_fix(float x) {
 constexpr int kFwdThreads = 512;
 constexpr int kStages = 4;
 
-template <int D, bool CAUSAL, int HG>
+template <int D, bool CAUSAL, int HG, bool KSPLIT>
 __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParams p) {
+  static_assert(!KSPLIT || CAUSAL, "the key split only balances causal work");
   constexpr int NW = kFwdThreads / 64;
   constexpr int WPH = NW / HG;       // wavefronts per query head
   constexpr int BMPOS = 32 * WPH;    // query positions per workgroup
-  constexpr int TILE = kBN * D;      // elements of one K or V tile
+  // Key split: wavefronts w and w + NW/2 own the same 32 query rows and take
+  // the first and the second 64 keys of every 128-key tile; their partial
+  // (m, l, acc) are merged at the end of each pass.  Two LDS stages of
+  // 128-key tiles take the place of four stages of 64-key tiles.
+  constexpr int BN = KSPLIT ? 2 * kBN : kBN;             // keys per tile
+  constexpr int STAGES = KSPLIT ? kStages / 2 : kStages;
+  constexpr int RPH = KSPLIT ? WPH / 2 : WPH;             // 32-row blocks per query head
+  constexpr int NPASS = KSPLIT ? 2 : 1;                   // passes over the keys
+  constexpr int TILE = BN * D;       // elements of one K or V tile
   constexpr int NC = D / 16;         // 16-deep steps of the Q.K product
   constexpr int ND = D / 32;         // 32-wide blocks of the output
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int NCOPY = TILE / 8 / kFwdThreads;   // 16-byte copies per thread per tile and tensor
-  static_assert(NCOPY >= 1, "tile too small for the workgroup");
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * kStages * TILE];   // K0..K3 | V0..V3
+  static_assert(NCOPY >= 1 && TILE / 8 % kFwdThreads == 0, "tile does not split over the workgroup");
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * STAGES * TILE];   // K stages | V stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
+  const int kh = KSPLIT ? wave / (NW / 2) : 0;     // key half of every tile
+  const int rw = KSPLIT ? wave % (NW / 2) : wave;  // row block
 
   int x = blockIdx.x;
   const int grp = x % p.groups;
   x /= p.groups;
   const int kvh = x % p.Hkv;
   const int b = x / p.Hkv;
-  const int hq = kvh * p.g + grp * HG + wave / WPH;
-  // Rows of this wavefront: q0w .. q0w + 31.  When the grid is too small to
-  // even out causal work by itself (p.pair), a workgroup owns, per query
-  // head, two half-tiles of BMPOS/2 rows: light half-tile i (few visible
-  // keys) and the mirrored heavy half-tile nh-1-i, so every workgroup
-  // carries the same work; the two wavefronts that share a SIMD (w and w+4)
-  // always get one light and one heavy block.
-  int q0w, q_end;      // q_end: one past the workgroup's last row
-  bool active = true;  // false for the second copy of a middle half-tile
-  if (CAUSAL && p.pair) {
-    constexpr int HALF = BMPOS / 2;
-    const int nh = (p.Tq + HALF - 1) / HALF;
-    const int i = blockIdx.y;
-    const int hh = wave % WPH;
-    const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
-    const int ht = heavy ? nh - 1 - i : i;
-    active = !(heavy && ht == i);
-    q0w = ht * HALF + (hh % (WPH / 2)) * 32;
-    q_end = min(p.Tq, (nh - i) * HALF);
-  } else {   // causal without pairing: heaviest query tile first
-    const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-    q0w = qt * BMPOS + (wave % WPH) * 32;
-    q_end = min(p.Tq, (qt + 1) * BMPOS);
-  }
-  const int my_q = q0w + col;
+  const int hq = kvh * p.g + grp * HG + rw / RPH;
 
   const bf16* Qg = (const bf16*)p.q + (size_t)(b * p.Hq + hq) * p.Tq * D;
   const bf16* Kg = (const bf16*)p.k + (size_t)(b * p.Hkv + kvh) * p.Tk * D;
   const bf16* Vg = (const bf16*)p.v + (size_t)(b * p.Hkv + kvh) * p.Tk * D;
 
-  // This lane's query row as the B operand of S^T = K Q^T:
-  // qf[c] = q[my_q][16c + 8*half .. +8].
-  bf16x8 qf[NC];
-  {
-    const uint32_t sgn = p.negate_q ? 0x80008000u : 0u;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (my_q < p.Tq) w = *(const u32x4*)(Qg + (size_t)my_q * D + 16 * c + 8 * half);
-      w ^= sgn;
-      __builtin_memcpy(&qf[c], &w, sizeof(w));
+  // Rows of this wavefront in pass `pass`: q0w .. q0w + 31; q_end is one past
+  // the workgroup's last row in that pass.
+  //  * Causal with many workgroups per compute unit: one pass; the hardware
+  //    dispatcher evens out the triangle, heaviest query tile first.
+  //  * Causal grids under 4 workgroups per compute unit (p.pair): a
+  //    workgroup owns, per query head, two half-tiles of BMPOS/2 rows, light
+  //    half-tile i (few visible keys) and the mirrored heavy half-tile
+  //    nh-1-i, so every workgroup carries the same work.
+  //    - Key split (up to about one such workgroup per compute unit): the
+  //      heavy half-tile in one pass and the light one in the other
+  //      (skipped when both are the middle one), both wavefronts of a SIMD
+  //      busy through both passes.
+  //    - Otherwise one pass; the two wavefronts that share a SIMD (w and
+  //      w+4) get one light and one heavy block.
+  int q0w = 0, q_end = 0;
+  bool active = true;  // false: nothing to compute in this pass
+  auto set_rows = [&](int pass) {
+    if constexpr (KSPLIT) {
+      constexpr int HALF = BMPOS / 2;
+      const int nh = (p.Tq + HALF - 1) / HALF;
+      const int i = blockIdx.y;
+      const int ht = pass == 0 ? nh - 1 - i : i;
+      active = pass == 0 || ht != nh - 1 - i;
+      q0w = ht * HALF + (rw % RPH) * 32;
+      q_end = min(p.Tq, (ht + 1) * HALF);
+    } else if (CAUSAL && p.pair) {
+      constexpr int HALF = BMPOS / 2;
+      const int nh = (p.Tq + HALF - 1) / HALF;
+      const int i = blockIdx.y;
+      const int hh = wave % WPH;
+      const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
+      const int ht = heavy ? nh - 1 - i : i;
+      active = !(heavy && ht == i);
+      q0w = ht * HALF + (hh % (WPH / 2)) * 32;
+      q_end = min(p.Tq, (nh - i) * HALF);
+    } else {
+      const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+      q0w = qt * BMPOS + (wave % WPH) * 32;
+      q_end = min(p.Tq, (qt + 1) * BMPOS);
     }
-  }
-
-  // Causal: row i sees key j iff j <= i + off (off = 0 top-left, Tk - Tq
-  // bottom-right).  Keys this workgroup needs: all, or under the causal mask
-  // those at or before its last (real) query row's limit.
-  const int off = p.causal_off;
-  const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
-  const int ntiles = (kend + kBN - 1) / kBN;
-  // Last key tile this wavefront computes (its rows see no key after it).
-  const int my_tiles = !active ? 0
-                       : CAUSAL ? (q0w + 31 + off < 0 ? 0 : min(ntiles, (q0w + 31 + off) / kBN + 1))
-                                : ntiles;
-  // A row that sees no key at all (bottom-right with Tq > Tk) keeps m = -inf;
-  // its rescale factor is 1 and its exponent offset 0, so it stays at 0.
-  const bool has_keys = !CAUSAL || my_q + off >= 0;
+  };
+  const int off = p.causal_off;   // causal: row i sees key j iff j <= i + off
 
   // Global->LDS copies through buffer resources covering this head's K and
   // V: reads past the last key return zeros (finite; those keys are masked).
@@ -238,11 +240,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     ksrc[r] = (uint32_t)(row * D + ((pc ^ k_swz<D>(row)) << 3)) * 2u;
     vsrc[r] = (uint32_t)(row * D + ((pc ^ v_swz<D>(row)) << 3)) * 2u;
   }
-  auto issue_copies = [&](int t) {   // tile t into stage t % kStages
-    const int st = t % kStages;
-    const uint32_t soff = (uint32_t)t * kBN * D * 2;
+  auto issue_copies = [&](int t) {   // tile t into stage t % STAGES
+    const int st = t % STAGES;
+    const uint32_t soff = (uint32_t)t * BN * D * 2;
     bf16* Kd = lds + st * TILE;
-    bf16* Vd = lds + (kStages + st) * TILE;
+    bf16* Vd = lds + (STAGES + st) * TILE;
 #pragma unroll
     for (int r = 0; r < NCOPY; ++r) {
       copy16_buf_to_lds(krsrc, Kd + (r * NW + wave) * 512, ksrc[r] + soff, 0);
@@ -260,18 +262,20 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   };
 
-  // K operand read bases (stage 0, key block 0): stage s adds s*TILE and key
-  // block kb adds 32*kb*D elements.  k_swz of rows 32*kb + col is k_swz(col).
+  // K operand read bases (stage 0, key block 0 of this wavefront's keys):
+  // stage s adds s*TILE and key block kb adds 32*kb*D elements.  k_swz of
+  // rows 64*kh + 32*kb + col is k_swz(col).
   uint32_t kread[NC];
   {
     const int sw = k_swz<D>(col);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) kread[cc] = lds_addr(lds + col * D + (((2 * cc + half) ^ sw) << 3));
+    for (int cc = 0; cc < NC; ++cc)
+      kread[cc] = lds_addr(lds + (64 * kh + col) * D + (((2 * cc + half) ^ sw) << 3));
   }
   // V operand bases for the transposing reads: input lane 4j + q of 16-lane
   // group G addresses 4 head-dim values starting at 32*db + 16*(G%2) + 4q
-  // of key row 4*half + j (+ 32*kb + 16*j2 + 8*hi, a compile-time offset);
-  // v_swz is the same for all of those rows.
+  // of key row 64*kh + 4*half + j (+ 32*kb + 16*j2 + 8*hi, a compile-time
+  // offset); v_swz is the same for all of those rows.
   uint32_t vread[ND];
   {
     const int tr_j = (lane & 15) >> 2;
@@ -281,193 +285,269 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int dd = 32 * db + tr_d;
-      vread[db] = lds_addr(lds + kStages * TILE + r0 * D + (((dd >> 3) ^ sw) << 3) + (dd & 7));
+      vread[db] = lds_addr(lds + STAGES * TILE + (64 * kh + r0) * D + (((dd >> 3) ^ sw) << 3) + (dd & 7));
     }
   }
 
   const float c = p.c;
-  // Probabilities are taken against a reference max that moves only when
-  // some row's max exceeds its reference by more than 2^kLazyLog2 in
-  // probability (see the update below).  nmc = -reference * c, and thr is
-  // the raw score past which the reference must move.  A row with no key
-  // at all keeps nmc = 0; +inf makes the first rescale factor exactly 0.
   const float lazy_raw = kLazyLog2 / c;
-  float m = kNegInf;   // running max of this row's raw scores
-  float nmc = has_keys ? __builtin_inff() : 0.f;
-  float thr = kNegInf;
-  float l = 0.f;       // this half-wave's share of the running sum
-  f32x16 acc[ND];
+  const uint32_t qsgn = p.negate_q ? 0x80008000u : 0u;
+
+  for (int pass = 0; pass < NPASS; ++pass) {
+    set_rows(pass);
+    if (KSPLIT && !active) break;   // the same for the whole workgroup
+    const int my_q = q0w + col;
+
+    // This lane's query row as the B operand of S^T = K Q^T:
+    // qf[c] = q[my_q][16c + 8*half .. +8].
+    bf16x8 qf[NC];
 #pragma unroll
-  for (int i = 0; i < ND; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  for (int t = 0; t < min(ntiles, kStages - 1); ++t) issue_copies(t);
-
-  // One key tile; ST = t % kStages is a compile-time constant, so every LDS
-  // operand address is a per-lane base plus an immediate offset.
-  auto tile = [&](int t, auto st_c) {
-    constexpr int ST = decltype(st_c)::value;
-    const int t0 = t * kBN;
-    wait_copies(min(ntiles - 1 - t, kStages - 2));
-    tile_barrier();   // tile t visible to all; stage (t-1) % kStages free
-    if (t + kStages - 1 < ntiles) issue_copies(t + kStages - 1);
-    if (t >= my_tiles) return;   // still copies and meets the barriers
-
-    // S^T for the tile's two 32-key blocks (on the diagonal tile a block may
-    // be entirely masked; it is computed anyway and masked below).  K
-    // operand I = 2*cc + kb is read PF operands ahead of its instruction;
-    // the two key blocks alternate so that consecutive instructions are
-    // independent.
-    f32x16 s[2];
-    {
-      constexpr int NF = 2 * NC;
-      constexpr int PF = NF < 8 ? NF : 8;
-      bf16x8 kf[NF];
-      auto read_k = [&](auto i_c) {
-        constexpr int I = decltype(i_c)::value;
-        kf[I] = lds_read_b128<(ST * TILE + (I & 1) * 32 * D) * 2>(kread[I >> 1]);
-      };
-      static_for<0, PF>(read_k);
-      static_for<0, NF>([&](auto i_c) {
-        constexpr int I = decltype(i_c)::value;
-        constexpr int AFTER = I + PF <= NF ? PF - 1 : NF - 1 - I;
-        lds_wait_tie<AFTER>(kf[I]);
-        s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? f32x16{} : s[I & 1]);
-        if constexpr (I + PF < NF) read_k(IC<I + PF>{});
-      });
+    for (int cc = 0; cc < NC; ++cc) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (my_q < p.Tq) w = *(const u32x4*)(Qg + (size_t)my_q * D + 16 * cc + 8 * half);
+      w ^= qsgn;
+      __builtin_memcpy(&qf[cc], &w, sizeof(w));
     }
 
-    // Mask (only tiles that cross the diagonal or the key tail): -inf
-    // before the max, so masked keys get probability exactly 0.
-    const bool need_mask = (t0 + kBN > p.Tk) || (CAUSAL && t0 + kBN - 1 > q0w + off);
-    if (need_mask) {
+    // Keys this workgroup needs: all, or under the causal mask those at or
+    // before its last (real) query row's limit.
+    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
+    const int ntiles = (kend + BN - 1) / BN;
+    // Last tile this wavefront computes: its rows see none of its keys
+    // after it.
+    const int lim = q0w + 31 + off - 64 * kh;
+    const int my_tiles = !active ? 0 : CAUSAL ? (lim < 0 ? 0 : min(ntiles, lim / BN + 1)) : ntiles;
+
+    // Probabilities are taken against a reference max that moves only when
+    // some row's max exceeds its reference by more than 2^kLazyLog2 in
+    // probability (see the update below).  nmc = -reference * c (0 until
+    // the row has seen a key), and thr is the raw score past which the
+    // reference must move.
+    float m = kNegInf;   // running max of this row's raw scores
+    float nmc = 0.f;
+    float thr = kNegInf;
+    float l = 0.f;       // this half-wave's share of the running sum
+    f32x16 acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+    for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
+
+    // One key tile; ST = t % STAGES is a compile-time constant, so every
+    // LDS operand address is a per-lane base plus an immediate offset.
+    auto tile = [&](int t, auto st_c) {
+      constexpr int ST = decltype(st_c)::value;
+      const int t0 = t * BN + 64 * kh;   // this wavefront's first key
+      wait_copies(min(ntiles - 1 - t, STAGES - 2));
+      tile_barrier();   // tile t visible to all; stage (t-1) % STAGES free
+      if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
+      if (t >= my_tiles) return;   // still copies and meets the barriers
+
+      // S^T for the wavefront's two 32-key blocks (on the diagonal tile a
+      // block may be entirely masked; it is computed anyway and masked
+      // below).  K operand I = 2*cc + kb is read PF operands ahead of its
+      // instruction; the two key blocks alternate so that consecutive
+      // instructions are independent.
+      f32x16 s[2];
+      {
+        constexpr int NF = 2 * NC;
+        constexpr int PF = NF < 8 ? NF : 8;
+        bf16x8 kf[NF];
+        auto read_k = [&](auto i_c) {
+          constexpr int I = decltype(i_c)::value;
+          kf[I] = lds_read_b128<(ST * TILE + (I & 1) * 32 * D) * 2>(kread[I >> 1]);
+        };
+        static_for<0, PF>(read_k);
+        static_for<0, NF>([&](auto i_c) {
+          constexpr int I = decltype(i_c)::value;
+          constexpr int AFTER = I + PF <= NF ? PF - 1 : NF - 1 - I;
+          lds_wait_tie<AFTER>(kf[I]);
+          s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? f32x16{} : s[I & 1]);
+          if constexpr (I + PF < NF) read_k(IC<I + PF>{});
+        });
+      }
+
+      // Mask (only blocks that cross the diagonal or the key tail): -inf
+      // before the max, so masked keys get probability exactly 0.
+      const bool need_mask = (t0 + 64 > p.Tk) || (CAUSAL && t0 + 63 > q0w + off);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
+            s[kb][r] = vis ? s[kb][r] : kNegInf;
+          }
+      }
+
+      // Row max of the tile: a chain of 3-input maxima in-lane, then across
+      // the two wave halves.
+      float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int i = 2; i < 32; i += 2)
+        mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
+      mt = max_halves(mt);
+
+      // Online update.  The running max m is exact; the reference the
+      // probabilities are taken against moves to it only when some row of
+      // the wavefront has outgrown its reference by more than 2^kLazyLog2
+      // ([FUSED07] "FlashAttention-2": rescale only when the maximum has
+      // increased; here only when it has increased by that much).  Between
+      // moves a probability may exceed 1 (by at most 2^kLazyLog2), which
+      // fp32 and bf16 represent with the same relative precision.  A row
+      // that has seen no key keeps nmc = 0, so its masked scores give 0.
+      const float m_prev = m;
+      m = fmaxf(m, mt);
+      if (__builtin_amdgcn_ballot_w64(m > thr) != 0) {
+        const float nmc_new = m > kNegInf ? -m * c : 0.f;
+        // Rows without a previous key hold acc = l = 0 and take factor 0;
+        // the others also undo the bf16 rounding of their largest
+        // probability so far (see top_fix).
+        const bool seen = m_prev > kNegInf;
+        const float corr = seen ? exp2_fast(nmc_new - nmc) : 0.f;
+        const float fold = seen ? top_fix(exp2_fast(fmaf(m_prev, c, nmc))) : 1.f;
+        const float f = corr * fold;
+#pragma unroll
+        for (int i = 0; i < ND; ++i) acc[i] *= f;
+        l *= corr;
+        nmc = nmc_new;
+        thr = m + lazy_raw;
+      }
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
-          s[kb][r] = vis ? s[kb][r] : kNegInf;
+          s[kb][r] = exp2_fast(fmaf(s[kb][r], c, nmc));
+          ls[r & 3] += s[kb][r];
         }
-    }
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
-    // Row max of the tile: a chain of 3-input maxima in-lane, then across
-    // the two wave halves.
-    float mt = fmaxf(s[0][0], s[0][1]);
+      // O^T += V^T P^T in four groups g = (kb, j2).  The B operand for keys
+      // {16*j2 + 4*half + 0..3, 16*j2 + 8 + 4*half + 0..3} of block kb is
+      // s[kb][8*j2 .. 8*j2+7]; the A operand holds V at the same keys for
+      // head-dim rows 32*db + col, read transposed from the row-major tile.
+      // The reads of group g+1 are in flight while group g multiplies.  A
+      // block that is entirely masked has probabilities 0 and is multiplied
+      // anyway (this happens only on the diagonal tile).
+      auto issue_v = [&](auto g_c, u32x2 (&v)[ND][2]) {
+        constexpr int G = decltype(g_c)::value;
+        constexpr int OFF = (ST * TILE + (32 * (G >> 1) + 16 * (G & 1)) * D) * 2;
+        static_for<0, ND>([&](auto db_c) {
+          constexpr int DB = decltype(db_c)::value;
+          v[DB][0] = lds_read_tr<OFF>(vread[DB]);
+          v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vread[DB]);
+        });
+      };
+      auto multiply = [&](auto g_c, u32x2 (&v)[ND][2]) {
+        constexpr int G = decltype(g_c)::value;
+        constexpr int KB = G >> 1, J2 = G & 1;
+        bf16x8 pb;
 #pragma unroll
-    for (int i = 2; i < 32; i += 2)
-      mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
-    mt = max_halves(mt);
-
-    // Online update.  The running max m is exact; the reference the
-    // probabilities are taken against moves to it only when some row of the
-    // wavefront has outgrown its reference by more than 2^kLazyLog2
-    // ([FUSED07] "FlashAttention-2": rescale only when the maximum has
-    // increased; here only when it has increased by that much).  Between
-    // moves a probability may exceed 1 (by at most 2^kLazyLog2), which fp32
-    // and bf16 represent with the same relative precision.
-    const float m_prev = m;
-    m = fmaxf(m, mt);
-    if (__builtin_amdgcn_ballot_w64(m > thr) != 0) {
-      const float nmc_new = has_keys ? -m * c : 0.f;
-      const float corr = has_keys ? exp2_fast(nmc_new - nmc) : 1.f;
-      // The bf16 rounding of the largest probability so far, undone: see
-      // top_fix.  Rows without a previous key take 1.
-      const float fold = m_prev > kNegInf ? top_fix(exp2_fast(fmaf(m_prev, c, nmc))) : 1.f;
-      const float f = corr * fold;
+        for (int i = 0; i < 8; i += 2) {
+          const bf16x2 two = to_bf16x2(s[KB][8 * J2 + i], s[KB][8 * J2 + i + 1]);
+          pb[i] = two[0];
+          pb[i + 1] = two[1];
+        }
 #pragma unroll
-      for (int i = 0; i < ND; ++i) acc[i] *= f;
-      l *= corr;
-      nmc = nmc_new;
-      thr = m + lazy_raw;
-    }
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = exp2_fast(fmaf(s[kb][r], c, nmc));
-        ls[r & 3] += s[kb][r];
+        for (int db = 0; db < ND; ++db) {
+          const u32x4 w = {v[db][0][0], v[db][0][1], v[db][1][0], v[db][1][1]};
+          bf16x8 a;
+          __builtin_memcpy(&a, &w, sizeof(a));
+          acc[db] = mma_32x32x16(a, pb, acc[db]);
+        }
+      };
+      {
+        constexpr int NR = 2 * ND;   // LDS reads per group
+        u32x2 va[ND][2], vb[ND][2];
+        issue_v(IC<0>{}, va);
+        issue_v(IC<1>{}, vb);
+        lds_tr_wait<NR>(va);
+        multiply(IC<0>{}, va);
+        issue_v(IC<2>{}, va);
+        lds_tr_wait<NR>(vb);
+        multiply(IC<1>{}, vb);
+        issue_v(IC<3>{}, vb);
+        lds_tr_wait<NR>(va);
+        multiply(IC<2>{}, va);
+        lds_tr_wait<0>(vb);
+        multiply(IC<3>{}, vb);
       }
-    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-
-    // O^T += V^T P^T in four groups g = (kb, j2).  The B operand for keys
-    // {16*j2 + 4*half + 0..3, 16*j2 + 8 + 4*half + 0..3} of block kb is
-    // s[kb][8*j2 .. 8*j2+7]; the A operand holds V at the same keys for
-    // head-dim rows 32*db + col, read transposed from the row-major tile.
-    // The reads of group g+1 are in flight while group g multiplies.  A
-    // block that is entirely masked has probabilities 0 and is multiplied
-    // anyway (this happens only on the diagonal tile).
-    auto issue_v = [&](auto g_c, u32x2 (&v)[ND][2]) {
-      constexpr int G = decltype(g_c)::value;
-      constexpr int OFF = (ST * TILE + (32 * (G >> 1) + 16 * (G & 1)) * D) * 2;
-      static_for<0, ND>([&](auto db_c) {
-        constexpr int DB = decltype(db_c)::value;
-        v[DB][0] = lds_read_tr<OFF>(vread[DB]);
-        v[DB][1] = lds_read_tr<OFF + 8 * D * 2>(vread[DB]);
+    };
+    for (int t = 0; t < ntiles; t += STAGES) {
+      static_for<0, STAGES>([&](auto s_c) {
+        if (t + decltype(s_c)::value < ntiles) tile(t + decltype(s_c)::value, s_c);
       });
-    };
-    auto multiply = [&](auto g_c, u32x2 (&v)[ND][2]) {
-      constexpr int G = decltype(g_c)::value;
-      constexpr int KB = G >> 1, J2 = G & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const bf16x2 two = to_bf16x2(s[KB][8 * J2 + i], s[KB][8 * J2 + i + 1]);
-        pb[i] = two[0];
-        pb[i + 1] = two[1];
-      }
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const u32x4 w = {v[db][0][0], v[db][0][1], v[db][1][0], v[db][1][1]};
-        bf16x8 a;
-        __builtin_memcpy(&a, &w, sizeof(a));
-        acc[db] = mma_32x32x16(a, pb, acc[db]);
-      }
-    };
-    {
-      constexpr int NR = 2 * ND;   // LDS reads per group
-      u32x2 va[ND][2], vb[ND][2];
-      issue_v(IC<0>{}, va);
-      issue_v(IC<1>{}, vb);
-      lds_tr_wait<NR>(va);
-      multiply(IC<0>{}, va);
-      issue_v(IC<2>{}, va);
-      lds_tr_wait<NR>(vb);
-      multiply(IC<1>{}, vb);
-      issue_v(IC<3>{}, vb);
-      lds_tr_wait<NR>(va);
-      multiply(IC<2>{}, va);
-      lds_tr_wait<0>(vb);
-      multiply(IC<3>{}, vb);
     }
-  };
-  for (int t = 0; t < ntiles; t += kStages) {
-    tile(t, IC<0>{});
-    if (t + 1 < ntiles) tile(t + 1, IC<1>{});
-    if (t + 2 < ntiles) tile(t + 2, IC<2>{});
-    if (t + 3 < ntiles) tile(t + 3, IC<3>{});
-  }
 
-  // Finalise: one division per row, with the rounding of the row's largest
-  // probability undone (top_fix); lse in natural log.
-  const float lt = sum_halves(l);
-  const float fix = lt > 0.f ? top_fix(exp2_fast(fmaf(m, c, nmc))) : 1.f;
-  const float inv = lt > 0.f ? fix / lt : 0.f;
-  if (active && my_q < p.Tq) {
-    bf16* Og = (bf16*)p.o + ((size_t)(b * p.Hq + hq) * p.Tq + my_q) * D;
+    // The bf16 rounding of the row's largest probability, undone (top_fix):
+    // folded into the final scale, or applied before the key halves merge.
+    const float fix = m > kNegInf ? top_fix(exp2_fast(fmaf(m, c, nmc))) : 1.f;
+    if constexpr (KSPLIT) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+      for (int i = 0; i < ND; ++i) acc[i] *= fix;
+    }
+
+    if constexpr (KSPLIT) {
+      // The two key halves of the same rows combine by the rescale rule
+      // against the larger of their references: the second-half wavefront
+      // hands its (m, nmc, l, acc) over through LDS (one 16-byte vector per
+      // lane and slot, so the accesses are conflict-free).  Every tile of
+      // the pass has been consumed and no copy is in flight (with two
+      // stages each tile waits for all copies issued before it).
+      tile_barrier();
+      f32x4* xch = (f32x4*)lds + rw * (4 * ND + 1) * 64 + lane;
+      if (kh == 1) {
+        xch[0] = f32x4{m, nmc, l, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 lo = to_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
-        const bf16x2 hi = to_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-        *(bf16x4*)(Og + 32 * db + 8 * j + 4 * half) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xch[(1 + 4 * db + j) * 64] = f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2],
+                                               acc[db][4 * j + 3]};
       }
-    if (p.lse != nullptr && half == 0)
-      p.lse[(size_t)(b * p.Hq + hq) * p.Tq + my_q] =
-          lt > 0.f ? (__builtin_amdgcn_logf(lt) - nmc) * kLn2 : kNegInf;
+      tile_barrier();
+      if (kh == 0) {
+        const f32x4 o = xch[0];
+        const bool la = m > kNegInf, lb = o[0] > kNegInf;
+        const float nmc_r = la && lb ? fminf(nmc, o[1]) : la ? nmc : o[1];
+        const float fa = la ? exp2_fast(nmc_r - nmc) : 0.f;
+        const float fb = lb ? exp2_fast(nmc_r - o[1]) : 0.f;
+        l = l * fa + o[2] * fb;
+        m = fmaxf(m, o[0]);
+        nmc = nmc_r;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 o2 = xch[(1 + 4 * db + j) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * j + e] = acc[db][4 * j + e] * fa + o2[e] * fb;
+          }
+      }
+      tile_barrier();   // the exchange slots are free before the next pass's copies
+    }
+
+    // Finalise: one division per row; lse in natural log.
+    const float lt = sum_halves(l);
+    const float inv = lt > 0.f ? (KSPLIT ? 1.f : fix) / lt : 0.f;
+    if (active && kh == 0 && my_q < p.Tq) {
+      bf16* Og = (bf16*)p.o + ((size_t)(b * p.Hq + hq) * p.Tq + my_q) * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 lo = to_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
+          const bf16x2 hi = to_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+          *(bf16x4*)(Og + 32 * db + 8 * j + 4 * half) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+        }
+      if (p.lse != nullptr && half == 0)
+        p.lse[(size_t)(b * p.Hq + hq) * p.Tq + my_q] =
+            lt > 0.f ? (__builtin_amdgcn_logf(lt) - nmc) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -598,6 +678,16 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(const FwdParams p) {
   }
 }
 
+template <int D, bool CAUSAL, bool KSPLIT>
+void launch_bf16_grid(int hg, dim3 grid, const FwdParams& p, hipStream_t stream) {
+  if (hg == 4)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4, KSPLIT>), grid, dim3(kFwdThreads), 0, stream, p);
+  else if (hg == 2)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2, KSPLIT>), grid, dim3(kFwdThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1, KSPLIT>), grid, dim3(kFwdThreads), 0, stream, p);
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bf16_hg(const FwdParams& p0, hipStream_t stream) {
   FwdParams p = p0;
@@ -605,24 +695,28 @@ hipError_t launch_bf16_hg(const FwdParams& p0, hipStream_t stream) {
   p.groups = p.g / hg;
   const int bmpos = 32 * (kFwdThreads / 64) / hg;
   const int nx = p.B * p.Hkv * p.groups;
-  int ny = (p.Tq + bmpos - 1) / bmpos;
+  const int ny = (p.Tq + bmpos - 1) / bmpos;
   // Causal work per query tile grows with its position.  With many
   // workgroups per compute unit the hardware dispatcher evens that out
   // (heaviest first); with fewer, each workgroup takes a light and the
-  // mirrored heavy half-tile instead.
+  // mirrored heavy half-tile.  Up to about one such workgroup per compute
+  // unit it does them one after the other with the key split (measured
+  // 5-14% faster there, 3% slower at two per compute unit).
   p.pair = 0;
   if (CAUSAL && (long long)nx * ny < 4LL * compute_units()) {
     const int half = bmpos / 2;
-    ny = ((p.Tq + half - 1) / half + 1) / 2;
+    const int nyp = ((p.Tq + half - 1) / half + 1) / 2;
+    const dim3 grid((unsigned)nx, (unsigned)nyp);
     p.pair = 1;
+    if constexpr (CAUSAL) {
+      if (2LL * nx * nyp <= 3LL * compute_units())
+        launch_bf16_grid<D, true, true>(hg, grid, p, stream);
+      else
+        launch_bf16_grid<D, true, false>(hg, grid, p, stream);
+    }
+  } else {
+    launch_bf16_grid<D, CAUSAL, false>(hg, dim3((unsigned)nx, (unsigned)ny), p, stream);
   }
-  dim3 grid((unsigned)nx, (unsigned)ny);
-  if (hg == 4)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 4>), grid, dim3(kFwdThreads), 0, stream, p);
-  else if (hg == 2)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 2>), grid, dim3(kFwdThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, 1>), grid, dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

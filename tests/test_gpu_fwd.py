@@ -219,6 +219,30 @@ def test_full_size_workloads_sampled_rows(name):
         check("lse", L[b, h, rows], Lr, BF16_LSE_TOL)
 
 
+@pytest.mark.parametrize("shape", [
+    (1, 32, 8, 4096, 128, 3.0),   # 512 paired workgroups: light/heavy wavefront pairs
+    (1, 12, 12, 4096, 64, 1.0),   # 384 paired workgroups, d = 64: key split
+    (1, 16, 8, 2048, 128, 1.0),   # 128 paired workgroups: key split, GQA
+], ids=lambda s: "x".join(map(str, s)))
+def test_small_causal_grids_sampled_rows(shape):
+    """Causal grids under four workgroups per compute unit balance the
+    triangle by pairing light and heavy half-tiles, either with the key split
+    or with light/heavy wavefront pairs, depending on the grid size.  Both
+    schemes are checked on sampled rows of every head."""
+    B, Hq, Hkv, T, d, qm = shape
+    w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=T, Tk=T, d=d, causal=True, q_mult=qm, seed=21)
+    q, k, v = inputs.prefill_inputs(w)
+    say("fa_fwd bf16 small causal grid", shape)
+    O, L = run_bf16(q, k, v, True, w.scale)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    rng = np.random.default_rng(7)
+    for h in range(Hq):
+        rows = sorted(set(rng.choice(T, size=24, replace=False).tolist()) | {0, 31, 32, T // 2, T - 1})
+        Or, Lr = oracle.softmax_attention_rows(q, k, v, causal=True, scale=w.scale, b=0, h=h, rows=rows)
+        check("O", O[0, h, rows], Or, BF16_O_TOL)
+        check("lse", L[0, h, rows], Lr, BF16_LSE_TOL)
+
+
 def test_large_query_scale_stability():
     """Q x 100 ([FUSED07] task 07.2, requirement 4): finite, matches the oracle."""
     w = inputs.Prefill("t", B=1, Hq=4, Hkv=2, Tq=300, Tk=300, d=128, causal=True, q_mult=100.0,
