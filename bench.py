@@ -394,7 +394,7 @@ def main():
                    "Tk": w.Tk, "d": w.d, "causal": w.causal, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64, causal, 1>",
+                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64, causal, 1, no key split>",
                      "kernel_ms": round(ev_ms, 4)},
     }
     log(f"[bench] headline {value:.1f} TFLOP/s, kernel {ev_ms:.3f} ms")
