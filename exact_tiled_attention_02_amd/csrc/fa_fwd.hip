@@ -11,9 +11,12 @@
 // softmax: вывод" and "FlashAttention-2"): a workgroup owns a block of query
 // rows and streams the key/value sequence past it in tiles of 64 keys.  Per
 // tile and row it keeps the running max m, the running sum l and the
-// unnormalised output accumulator; when the max grows the old l and
-// accumulator are multiplied by 2^((m_old - m_new) * c).  O = acc / l is
-// written once at the end together with lse = m + log l.  Neither scores nor
+// unnormalised output accumulator; when the reference max moves the old l
+// and accumulator are multiplied by 2^((ref_old - ref_new) * c).  The bf16
+// kernel moves its reference only when a row's max has outgrown it by more
+// than a factor 2^8 and undoes the bf16 rounding of the largest probability
+// (top_fix), which keeps the exact-max result.  O = acc / l is written once
+// at the end together with lse = ref + log l.  Neither scores nor
 // probabilities ever leave the chip.
 //
 // Mapping onto CDNA4:
@@ -43,9 +46,11 @@
 //    visited; only tiles crossing the diagonal (or the key tail) are masked,
 //    with -inf before the max ([FUSED07] task 07.2 pitfalls).  The diagonal
 //    is top-left (row i sees keys j <= i) or, for a chunk of queries at the
-//    end of a cached sequence, bottom-right (j <= i + Tk - Tq).  A workgroup
-//    pairs a light and the mirrored heavy half-tile of query rows so that
-//    all workgroups carry the same work.
+//    end of a cached sequence, bottom-right (j <= i + Tk - Tq).  On small
+//    causal grids a workgroup pairs a light and the mirrored heavy half-tile
+//    of query rows so that all workgroups carry the same work, splitting
+//    the keys of every tile between wavefront pairs when the grid holds
+//    about one workgroup per compute unit.
 #include <type_traits>
 
 #include "fa_device.h"
