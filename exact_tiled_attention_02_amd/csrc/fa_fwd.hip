@@ -504,6 +504,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       // the pass has been consumed and no copy is in flight (with two
       // stages each tile waits for all copies issued before it).
       tile_barrier();
+      static_assert((NW / 2) * (4 * ND + 1) * 64 * 16 <= (int)sizeof(lds), "exchange exceeds LDS");
       f32x4* xch = (f32x4*)lds + rw * (4 * ND + 1) * 64 + lane;
       if (kh == 1) {
         xch[0] = f32x4{m, nmc, l, 0.f};

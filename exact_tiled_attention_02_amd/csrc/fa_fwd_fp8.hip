@@ -83,50 +83,78 @@ __device__ __forceinline__ float sum_halves8(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool CAUSAL, int HG>
+template <int D, bool CAUSAL, int HG, bool KSPLIT>
 __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams p) {
+  static_assert(!KSPLIT || CAUSAL, "the key split only balances causal work");
   constexpr int NW = kF8Threads / 64;
   constexpr int WPH = NW / HG;           // wavefronts per query head
   constexpr int BMPOS = 32 * WPH;        // query positions per workgroup
-  constexpr int TILE = kF8BN * D;        // bytes of one K or V tile
+  // Key split (small causal grids), as in the bf16 kernel: wavefronts w and
+  // w + NW/2 own the same rows and take the first and the second 64 keys of
+  // every 128-key tile, in two passes (heavy half-tile, then light), and
+  // merge their (m, l, acc) at the end of each pass.
+  constexpr int BN = KSPLIT ? 2 * kF8BN : kF8BN;            // keys per tile
+  constexpr int STAGES = KSPLIT ? kF8Stages / 2 : kF8Stages;
+  constexpr int RPH = KSPLIT ? WPH / 2 : WPH;               // 32-row blocks per query head
+  constexpr int NPASS = KSPLIT ? 2 : 1;
+  constexpr int TILE = BN * D;           // bytes of one K or V tile
   constexpr int NC8 = D / 64;            // 64-deep steps of the Q.K product
   constexpr int ND = D / 32;             // 32-wide blocks of the output
   constexpr int CPR = D / 16;            // 16-byte chunks per row
-  constexpr int CW = TILE / 1024;        // wavefronts that copy (one 16-byte chunk per lane)
-  static_assert(CW >= 1 && CW <= NW, "tile size and workgroup do not match");
-  static_assert((2 * kF8Stages - 1) * TILE + 48 * D < 65536, "operand offsets must fit the immediate");
-  __shared__ __attribute__((aligned(16))) char lds[2 * kF8Stages * TILE];   // K0..K3 | V0..V3
+  constexpr int CW = TILE / 1024;        // 1 KiB copy blocks per tile and tensor
+  constexpr int CWW = CW < NW ? CW : NW; // wavefronts that copy
+  constexpr int NCP = CW / CWW;          // copies per copying wavefront, tile and tensor
+  static_assert(CW >= 1 && CW % CWW == 0, "tile size and workgroup do not match");
+  static_assert((2 * STAGES - 1) * TILE + 48 * D < 65536, "operand offsets must fit the immediate");
+  // Key split: the merge hands (m, l) and the accumulator of NW/2 row blocks
+  // over through LDS, one 16-byte vector per lane and slot.
+  constexpr int XCH = KSPLIT ? (NW / 2) * (4 * ND + 1) * 64 * 16 : 0;
+  constexpr int LDS_BYTES = 2 * STAGES * TILE > XCH ? 2 * STAGES * TILE : XCH;
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];   // K stages | V stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int col = lane & 31;
+  const int kh = KSPLIT ? wave / (NW / 2) : 0;     // key half of every tile
+  const int rw = KSPLIT ? wave % (NW / 2) : wave;  // row block
 
   int x = blockIdx.x;
   const int grp = x % p.groups;
   x /= p.groups;
   const int kvh = x % p.Hkv;
   const int b = x / p.Hkv;
-  const int hq = kvh * p.g + grp * HG + wave / WPH;
-  int q0w, q_end;
+  const int hq = kvh * p.g + grp * HG + rw / RPH;
+  // Rows of pass `pass`, with the same pairing of light and heavy half-tiles
+  // as the bf16 kernel.
+  int q0w = 0, q_end = 0;
   bool active = true;
-  if (CAUSAL && p.pair) {   // same pairing as the bf16 kernel
-    constexpr int HALF = BMPOS / 2;
-    const int nh = (p.Tq + HALF - 1) / HALF;
-    const int i = blockIdx.y;
-    const int hh = wave % WPH;
-    const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
-    const int ht = heavy ? nh - 1 - i : i;
-    active = !(heavy && ht == i);
-    q0w = ht * HALF + (hh % (WPH / 2)) * 32;
-    q_end = min(p.Tq, (nh - i) * HALF);
-  } else {
-    const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-    q0w = qt * BMPOS + (wave % WPH) * 32;
-    q_end = min(p.Tq, (qt + 1) * BMPOS);
-  }
-  const int my_q = q0w + col;
+  auto set_rows = [&](int pass) __attribute__((always_inline)) {
+    if constexpr (KSPLIT) {
+      constexpr int HALF = BMPOS / 2;
+      const int nh = (p.Tq + HALF - 1) / HALF;
+      const int i = blockIdx.y;
+      const int ht = pass == 0 ? nh - 1 - i : i;
+      active = pass == 0 || ht != nh - 1 - i;
+      q0w = ht * HALF + (rw % RPH) * 32;
+      q_end = min(p.Tq, (ht + 1) * HALF);
+    } else if (CAUSAL && p.pair) {
+      constexpr int HALF = BMPOS / 2;
+      const int nh = (p.Tq + HALF - 1) / HALF;
+      const int i = blockIdx.y;
+      const int hh = wave % WPH;
+      const bool heavy = (wave >= 4) != ((WPH < 8) && (hh >= WPH / 2));
+      const int ht = heavy ? nh - 1 - i : i;
+      active = !(heavy && ht == i);
+      q0w = ht * HALF + (hh % (WPH / 2)) * 32;
+      q_end = min(p.Tq, (nh - i) * HALF);
+    } else {
+      const int qt = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+      q0w = qt * BMPOS + (wave % WPH) * 32;
+      q_end = min(p.Tq, (qt + 1) * BMPOS);
+    }
+  };
 
   const size_t qplane = (size_t)b * p.Hq + hq;
   const size_t kvplane = (size_t)b * p.Hkv + kvh;
@@ -134,80 +162,57 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
   const uint8_t* Kg = (const uint8_t*)p.k + kvplane * p.Tk * D;
   const uint8_t* Vg = (const uint8_t*)p.v + kvplane * p.Tk * D;
 
-  // This lane's query row as the B operand: 32 codes of head dimensions
-  // 64c + 32*half .. +32 (sign bits flipped for a negative scale).
-  i32x8 qf[NC8];
-  {
-    const uint32_t sgn = p.negate_q ? 0x80808080u : 0u;
-#pragma unroll
-    for (int c = 0; c < NC8; ++c) {
-      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-      if (my_q < p.Tq) {
-        const uint8_t* src = Qg + (size_t)my_q * D + 64 * c + 32 * half;
-        w0 = *(const u32x4*)src;
-        w1 = *(const u32x4*)(src + 16);
-      }
-      w0 ^= sgn;
-      w1 ^= sgn;
-      qf[c] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
-                    (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
-    }
-  }
-  // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks.
-  const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
-  const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
-  const float vs = p.vscale[kvplane];
-
   const int off = p.causal_off;
-  const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
-  const int ntiles = (kend + kF8BN - 1) / kF8BN;
-  const int my_tiles = !active ? 0
-                       : CAUSAL ? (q0w + 31 + off < 0 ? 0 : min(ntiles, (q0w + 31 + off) / kF8BN + 1))
-                                : ntiles;
-  const bool has_keys = !CAUSAL || my_q + off >= 0;
 
-  // Copies: wavefront w < CW fills LDS chunks [w*64, +64) of a tile; chunk
-  // L is row L / CPR at position L % CPR, holding chunk (L % CPR) ^ f8swz(row).
+  // Copies: copy r of wavefront w < CWW fills LDS bytes [(r*NW + w)*1024,
+  // +1024) of a tile; chunk L is row L / CPR at position L % CPR, holding
+  // chunk (L % CPR) ^ f8swz(row).
   const int nbytes = p.Tk * D;
   const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, nbytes, 0x00020000);
-  uint32_t csrc;
-  {
-    const int L = wave * 64 + lane;
+  uint32_t csrc[NCP];
+#pragma unroll
+  for (int r = 0; r < NCP; ++r) {
+    const int L = (r * NW + wave) * 64 + lane;
     const int row = L / CPR;
-    csrc = (uint32_t)(row * D + (((L % CPR) ^ f8swz<D>(row)) << 4));
+    csrc[r] = (uint32_t)(row * D + (((L % CPR) ^ f8swz<D>(row)) << 4));
   }
   auto issue_copies = [&](int t) __attribute__((always_inline)) {
-    if (wave >= CW) return;
-    const int st = t % kF8Stages;
+    if (wave >= CWW) return;
+    const int st = t % STAGES;
     const uint32_t soff = (uint32_t)t * TILE;
-    copy16_buf_to_lds(krsrc, lds + st * TILE + wave * 1024, csrc + soff, 0);
-    copy16_buf_to_lds(vrsrc, lds + (kF8Stages + st) * TILE + wave * 1024, csrc + soff, 0);
+#pragma unroll
+    for (int r = 0; r < NCP; ++r) {
+      copy16_buf_to_lds(krsrc, lds + st * TILE + (r * NW + wave) * 1024, csrc[r] + soff, 0);
+      copy16_buf_to_lds(vrsrc, lds + (STAGES + st) * TILE + (r * NW + wave) * 1024, csrc[r] + soff, 0);
+    }
   };
+  // The vector-memory counter counts 2*NCP per tile on a copying wavefront.
   auto wait_copies = [&](int later) __attribute__((always_inline)) {
     if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<4>());
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<4 * NCP>());
     else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2>());
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm<2 * NCP>());
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
   };
 
-  // K operand bases (stage 0, key block 0): row `col`, chunks 4c + 2*half
-  // and 4c + 2*half + 1 (c < NC8).
+  // K operand bases (stage 0, key block 0 of this wavefront's keys): row
+  // 64*kh + col, chunks 4c + 2*half and 4c + 2*half + 1 (c < NC8); f8swz
+  // does not see the 64-row offset.
   uint32_t kread[2 * NC8];
   {
     const int sw = f8swz<D>(col);
 #pragma unroll
     for (int i = 0; i < 2 * NC8; ++i) {
       const int ch = 4 * (i >> 1) + 2 * half + (i & 1);
-      kread[i] = lds_addr(lds) + col * D + ((ch ^ sw) << 4);
+      kread[i] = lds_addr(lds) + (64 * kh + col) * D + ((ch ^ sw) << 4);
     }
   }
   // V^T operand bases for the transposing reads: input lane 2e + h of
   // 16-lane group G addresses 8 codes, head dimensions 32*db + 16*(G%2) +
-  // 8h .. +8, of key row 8*(e/4) + 4*half + e%4 (plus 16j for read j, a
-  // compile-time offset that f8swz does not see).
+  // 8h .. +8, of key row 64*kh + 8*(e/4) + 4*half + e%4 (plus 16j for read
+  // j, a compile-time offset that f8swz does not see).
   uint32_t vread[ND];
   {
     const int t = lane & 15;
@@ -217,152 +222,235 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       const int ch = 2 * db + ((lane >> 4) & 1);
-      vread[db] = lds_addr(lds + kF8Stages * TILE) + row * D + ((ch ^ sw) << 4) + 8 * h;
+      vread[db] = lds_addr(lds + STAGES * TILE) + (64 * kh + row) * D + ((ch ^ sw) << 4) + 8 * h;
     }
   }
+  const float vs = p.vscale[kvplane];
+  const uint32_t qsgn = p.negate_q ? 0x80808080u : 0u;
 
-  float m = kNegInf;   // running max of this row's raw 8-bit products
-  float l = 0.f;       // this half-wave's share of the running sum of 448 * P
-  f32x16 acc[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  for (int pass = 0; pass < NPASS; ++pass) {
+    set_rows(pass);
+    if (KSPLIT && !active) break;   // the same for the whole workgroup
+    const int my_q = q0w + col;
 
-  for (int t = 0; t < min(ntiles, kF8Stages - 1); ++t) issue_copies(t);
-
-  auto tile = [&](int t, auto st_c) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    constexpr int KT = ST * TILE;
-    constexpr int VT = ST * TILE;   // vread already points at the V stages
-    const int t0 = t * kF8BN;
-    wait_copies(min(ntiles - 1 - t, kF8Stages - 2));
-    tile_barrier();
-    if (t + kF8Stages - 1 < ntiles) issue_copies(t + kF8Stages - 1);
-    if (t >= my_tiles) return;
-
-    // S^T for the two 32-key blocks.
-    u32x4 kr[2][2 * NC8];
-    static_for<0, 2 * NC8>([&](auto i_c) {
-      kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
-      kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
-    });
-    lgkm_wait<0>();
+    // This lane's query row as the B operand: 32 codes of head dimensions
+    // 64c + 32*half .. +32 (sign bits flipped for a negative scale).
+    i32x8 qf[NC8];
 #pragma unroll
-    for (int i = 0; i < 2 * NC8; ++i) {
-      tie(kr[0][i]);
-      tie(kr[1][i]);
-    }
-    f32x16 s[2] = {};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < NC8; ++c) {
-        const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
-        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        s[kb] = mma_f8(a, qf[c], s[kb]);
+    for (int c = 0; c < NC8; ++c) {
+      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+      if (my_q < p.Tq) {
+        const uint8_t* src = Qg + (size_t)my_q * D + 64 * c + 32 * half;
+        w0 = *(const u32x4*)src;
+        w1 = *(const u32x4*)(src + 16);
       }
+      w0 ^= qsgn;
+      w1 ^= qsgn;
+      qf[c] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
+                    (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
+    }
+    // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks.
+    const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
+    const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
 
-    // V^T reads for the first half of the output blocks go out now; they do
-    // not depend on the probabilities.
-    constexpr int NDH = ND / 2;
-    u32x2 va[ND][4];
-    static_for<0, NDH>([&](auto db_c) {
-      static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
-    });
+    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
+    const int ntiles = (kend + BN - 1) / BN;
+    const int lim = q0w + 31 + off - 64 * kh;   // last key its rows see, minus its block start
+    const int my_tiles = !active ? 0 : CAUSAL ? (lim < 0 ? 0 : min(ntiles, lim / BN + 1)) : ntiles;
+    // A row that sees no key keeps m = -inf, factor 1 and offset 0.  Under
+    // the key split the same holds, tile by tile, for a row whose key half
+    // has shown it no key yet.
+    const bool has_keys = !CAUSAL || my_q + off >= 0;
 
-    const bool need_mask = (t0 + kF8BN > p.Tk) || (CAUSAL && t0 + kF8BN - 1 > q0w + off);
-    if (need_mask) {
+    float m = kNegInf;   // running max of this row's raw 8-bit products
+    float l = 0.f;       // this half-wave's share of the running sum of 448 * P
+    f32x16 acc[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+    for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
+
+    auto tile = [&](int t, auto st_c) __attribute__((always_inline)) {
+      constexpr int ST = decltype(st_c)::value;
+      constexpr int KT = ST * TILE;
+      constexpr int VT = ST * TILE;   // vread already points at the V stages
+      const int t0 = t * BN + 64 * kh;   // this wavefront's first key
+      wait_copies(min(ntiles - 1 - t, STAGES - 2));
+      tile_barrier();
+      if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
+      if (t >= my_tiles) return;
+      // S^T for the two 32-key blocks.
+      u32x4 kr[2][2 * NC8];
+      static_for<0, 2 * NC8>([&](auto i_c) {
+        kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
+        kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
+      });
+      lgkm_wait<0>();
+#pragma unroll
+      for (int i = 0; i < 2 * NC8; ++i) {
+        tie(kr[0][i]);
+        tie(kr[1][i]);
+      }
+      f32x16 s[2] = {};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < NC8; ++c) {
+          const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          s[kb] = mma_f8(a, qf[c], s[kb]);
+        }
+
+      // V^T reads for the first half of the output blocks go out now; they do
+      // not depend on the probabilities.
+      constexpr int NDH = ND / 2;
+      u32x2 va[ND][4];
+      static_for<0, NDH>([&](auto db_c) {
+        static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
+      });
+
+      const bool need_mask = (t0 + 64 > p.Tk) || (CAUSAL && t0 + 63 > q0w + off);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
+            s[kb][r] = vis ? s[kb][r] : kNegInf;
+          }
+      }
+      float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+      for (int i = 2; i < 32; i += 2)
+        mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
+      mt = max_halves8(mt);
+      const float m_new = fmaxf(m, mt);
+      const bool live = KSPLIT ? m_new > kNegInf : has_keys;
+      const float corr = live ? exp2_fast((m - m_new) * cq) : 1.f;
+      if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+#pragma unroll
+        for (int i = 0; i < ND; ++i) acc[i] *= corr;
+      }
+      l *= corr;
+      m = m_new;
+      // 448 * P = 2^(s*cq - m*cq + log2 448): the row's largest probability
+      // becomes the largest E4M3 value.
+      const float mc = live ? m * cq - kLog2E4M3Max : 0.f;
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
-          s[kb][r] = vis ? s[kb][r] : kNegInf;
+          s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
+          ls[r & 3] += s[kb][r];
         }
-    }
-    float mt = fmaxf(s[0][0], s[0][1]);
+      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      // B operand: byte 4w + i is key block w/4, register 4*(w%4) + i.
+      i32x8 pb;
 #pragma unroll
-    for (int i = 2; i < 32; i += 2)
-      mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
-    mt = max_halves8(mt);
-    const float m_new = fmaxf(m, mt);
-    const float corr = has_keys ? exp2_fast((m - m_new) * cq) : 1.f;
-    if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-#pragma unroll
-      for (int i = 0; i < ND; ++i) acc[i] *= corr;
-    }
-    l *= corr;
-    m = m_new;
-    // 448 * P = 2^(s*cq - m*cq + log2 448): the row's largest probability
-    // becomes the largest E4M3 value.
-    const float mc = has_keys ? m * cq - kLog2E4M3Max : 0.f;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
-        ls[r & 3] += s[kb][r];
+      for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r = 4 * (w & 3);
+        pb[w] = pack_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
       }
-    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-    // B operand: byte 4w + i is key block w/4, register 4*(w%4) + i.
-    i32x8 pb;
+
+      lgkm_wait<0>();
+      static_for<NDH, ND>([&](auto db_c) {
+        static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
+      });
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int kb = w >> 2, r = 4 * (w & 3);
-      pb[w] = pack_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
+      for (int db = 0; db < NDH; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tie(va[db][j]);
+        const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
+                         (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
+        acc[db] = mma_f8(a, pb, acc[db]);
+      }
+      lgkm_wait<0>();
+#pragma unroll
+      for (int db = NDH; db < ND; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tie(va[db][j]);
+        const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
+                         (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
+        acc[db] = mma_f8(a, pb, acc[db]);
+      }
+    };
+    for (int t = 0; t < ntiles; t += STAGES) {
+      static_for<0, STAGES>([&](auto s_c) {
+        if (t + decltype(s_c)::value < ntiles) tile(t + decltype(s_c)::value, s_c);
+      });
     }
 
-    lgkm_wait<0>();
-    static_for<NDH, ND>([&](auto db_c) {
-      static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
-    });
+    if constexpr (KSPLIT) {
+      // The two key halves of the same rows combine by the rescale rule:
+      // the second-half wavefront hands its (m, l, acc) over through LDS (one
+      // 16-byte vector per lane and slot).  No copy is in flight: with two
+      // stages every tile waits for all copies issued before it.
+      tile_barrier();
+      f32x4* xch = (f32x4*)lds + rw * (4 * ND + 1) * 64 + lane;
+      if (kh == 1) {
+        xch[0] = f32x4{m, l, 0.f, 0.f};
 #pragma unroll
-    for (int db = 0; db < NDH; ++db) {
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) tie(va[db][j]);
-      const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
-                       (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
-      acc[db] = mma_f8(a, pb, acc[db]);
-    }
-    lgkm_wait<0>();
-#pragma unroll
-    for (int db = NDH; db < ND; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tie(va[db][j]);
-      const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
-                       (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
-      acc[db] = mma_f8(a, pb, acc[db]);
-    }
-  };
-  for (int t = 0; t < ntiles; t += kF8Stages) {
-    tile(t, IC<0>{});
-    if (t + 1 < ntiles) tile(t + 1, IC<1>{});
-    if (t + 2 < ntiles) tile(t + 2, IC<2>{});
-    if (t + 3 < ntiles) tile(t + 3, IC<3>{});
-  }
-
-  // O = acc * vs / l (the 448 of the probabilities cancels); lse in natural
-  // log: (m*cq + log2(l) - log2 448) * ln 2.
-  const float lt = sum_halves8(l);
-  const float inv = lt > 0.f ? vs / lt : 0.f;
-  if (active && my_q < p.Tq) {
-    bf16* Og = (bf16*)p.o + (qplane * p.Tq + my_q) * D;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x2 lo = to_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
-        const bf16x2 hi = to_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
-        *(bf16x4*)(Og + 32 * db + 8 * j + 4 * half) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+          for (int j = 0; j < 4; ++j)
+            xch[(1 + 4 * db + j) * 64] = f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2],
+                                               acc[db][4 * j + 3]};
       }
-    if (p.lse != nullptr && half == 0)
-      p.lse[qplane * p.Tq + my_q] =
-          lt > 0.f ? (m * cq + __builtin_amdgcn_logf(lt) - kLog2E4M3Max) * kLn2 : kNegInf;
+      tile_barrier();
+      if (kh == 0) {
+        const f32x4 o = xch[0];
+        const float m_new = fmaxf(m, o[0]);
+        const bool live = m_new > kNegInf;
+        const float fa = exp2_fast(live ? (m - m_new) * cq : 0.f);
+        const float fb = exp2_fast(live ? (o[0] - m_new) * cq : 0.f);
+        l = l * fa + o[1] * fb;
+        m = m_new;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 o2 = xch[(1 + 4 * db + j) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * j + e] = acc[db][4 * j + e] * fa + o2[e] * fb;
+          }
+      }
+      tile_barrier();   // the exchange slots are free before the next pass's copies
+    }
+
+    // O = acc * vs / l (the 448 of the probabilities cancels); lse in natural
+    // log: (m*cq + log2(l) - log2 448) * ln 2.
+    const float lt = sum_halves8(l);
+    const float inv = lt > 0.f ? vs / lt : 0.f;
+    if (active && kh == 0 && my_q < p.Tq) {
+      bf16* Og = (bf16*)p.o + (qplane * p.Tq + my_q) * D;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 lo = to_bf16x2(acc[db][4 * j] * inv, acc[db][4 * j + 1] * inv);
+          const bf16x2 hi = to_bf16x2(acc[db][4 * j + 2] * inv, acc[db][4 * j + 3] * inv);
+          *(bf16x4*)(Og + 32 * db + 8 * j + 4 * half) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3);
+        }
+      if (p.lse != nullptr && half == 0)
+        p.lse[qplane * p.Tq + my_q] =
+            lt > 0.f ? (m * cq + __builtin_amdgcn_logf(lt) - kLog2E4M3Max) * kLn2 : kNegInf;
+    }
   }
+}
+
+template <int D, bool CAUSAL, bool KSPLIT>
+void launch_fp8_grid(int hg, dim3 grid, const FwdParams& p, hipStream_t stream) {
+  if (hg == 4)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 4, KSPLIT>), grid, dim3(kF8Threads), 0, stream, p);
+  else if (hg == 2)
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 2, KSPLIT>), grid, dim3(kF8Threads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 1, KSPLIT>), grid, dim3(kF8Threads), 0, stream, p);
 }
 
 template <int D, bool CAUSAL>
@@ -372,20 +460,24 @@ hipError_t launch_fp8_hg(const FwdParams& p0, hipStream_t stream) {
   p.groups = p.g / hg;
   const int bmpos = 32 * (kF8Threads / 64) / hg;
   const int nx = p.B * p.Hkv * p.groups;
-  int ny = (p.Tq + bmpos - 1) / bmpos;
+  const int ny = (p.Tq + bmpos - 1) / bmpos;
+  // The same grid choice as the bf16 kernel: light/heavy pairing under four
+  // workgroups per compute unit, with the key split up to about one.
   p.pair = 0;
   if (CAUSAL && (long long)nx * ny < 4LL * compute_units()) {
     const int half = bmpos / 2;
-    ny = ((p.Tq + half - 1) / half + 1) / 2;
+    const int nyp = ((p.Tq + half - 1) / half + 1) / 2;
+    const dim3 grid((unsigned)nx, (unsigned)nyp);
     p.pair = 1;
+    if constexpr (CAUSAL) {
+      if (2LL * nx * nyp <= 3LL * compute_units())
+        launch_fp8_grid<D, true, true>(hg, grid, p, stream);
+      else
+        launch_fp8_grid<D, true, false>(hg, grid, p, stream);
+    }
+  } else {
+    launch_fp8_grid<D, CAUSAL, false>(hg, dim3((unsigned)nx, (unsigned)ny), p, stream);
   }
-  dim3 grid((unsigned)nx, (unsigned)ny);
-  if (hg == 4)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 4>), grid, dim3(kF8Threads), 0, stream, p);
-  else if (hg == 2)
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 2>), grid, dim3(kF8Threads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, 1>), grid, dim3(kF8Threads), 0, stream, p);
   return hipGetLastError();
 }
 
