@@ -200,9 +200,13 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 
   hipStream_t hs = (hipStream_t)stream;
   const size_t rows = (size_t)B * Hq * (size_t)Tqp;
+  // Small causal grids split each dK/dV key block over kparts workgroups,
+  // whose fp32 partials live in the workspace after the row terms.
+  const int kparts = Tk > 0 ? fa::bwd_key_parts(B, Hkv, Tk, causal != 0) : 1;
+  const size_t pfl = kparts > 1 ? (size_t)kparts * B * Hkv * (size_t)Tk * d : 0;   // floats per tensor
   char* ws = nullptr;
-  if (rows > 0) {
-    const int wst = workspace(hs, 2 * rows * sizeof(float), &ws);
+  if (rows > 0 || pfl > 0) {
+    const int wst = workspace(hs, (2 * rows + 2 * pfl) * sizeof(float), &ws);
     if (wst != FA_OK) return wst;
   }
   fa::BwdParams p{};
@@ -215,8 +219,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.l2 = (float*)ws;
-  p.delta = ws != nullptr ? (float*)ws + rows : nullptr;
+  p.l2 = rows > 0 ? (float*)ws : nullptr;
+  p.delta = rows > 0 ? (float*)ws + rows : nullptr;
+  p.kparts = kparts;
+  p.part_dk = pfl > 0 ? (float*)ws + 2 * rows : nullptr;
+  p.part_dv = pfl > 0 ? (float*)ws + 2 * rows + pfl : nullptr;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

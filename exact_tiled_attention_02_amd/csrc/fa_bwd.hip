@@ -168,6 +168,14 @@ __device__ __forceinline__ void store_acc_row(bf16* dst_row, int db, int half, c
   }
 }
 
+// The same row of an accumulator as fp32, unscaled (a partial sum).
+template <int D>
+__device__ __forceinline__ void store_acc_row_f32(float* dst_row, int db, int half, const f32x16& a) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *(f32x4*)(dst_row + 32 * db + 8 * j + 4 * half) = f32x4{a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]};
+}
+
 // ---------------------------------------------------------------------------
 // 1. Row terms: D_i = dO_i . O_i and L_i * log2(e)
 // ---------------------------------------------------------------------------
@@ -224,10 +232,12 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   const int half = lane >> 5;
   const int col = lane & 31;
 
-  // Heaviest key blocks (the first ones, under the causal mask) first.
+  // Heaviest key blocks (the first ones, under the causal mask) first; the
+  // kparts parts of a block are neighbours.
   const int nbkv = p.B * p.Hkv;
   const int bkv = blockIdx.x % nbkv;
-  const int kblk = blockIdx.x / nbkv;
+  const int kblk = blockIdx.x / nbkv / p.kparts;
+  const int part = blockIdx.x / nbkv % p.kparts;
   const int b = bkv / p.Hkv;
   const int kvh = bkv % p.Hkv;
   const int k0 = kblk * kKeysPerWg;
@@ -256,6 +266,9 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
   const int qs = CAUSAL ? max(0, k0 - off) / kQTile * kQTile : 0;
   const int ntq = qs < p.Tq ? (p.Tq - qs + kQTile - 1) / kQTile : 0;
   const int nit = p.g * ntq;
+  // This workgroup's items (query head it / ntq, query tile it % ntq).
+  const int i0 = (int)((long long)nit * part / p.kparts);
+  const int i1 = (int)((long long)nit * (part + 1) / p.kparts);
 
   // Copy r of wavefront w fills LDS chunks [(r*NW + w)*64, +64) of a tile:
   // chunk L is row L / CPR at position L % CPR, holding chunk
@@ -407,7 +420,7 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
     // all meet), and nobody reads stage ST^1 any more.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
     tile_barrier();
-    if (it + 1 < nit) issue(it + 1, IC<ST ^ 1>{});
+    if (it + 1 < i1) issue(it + 1, IC<ST ^ 1>{});
     const int q0 = qs + (it % ntq) * kQTile;
     static_for<0, 2>([&](auto hf_c) {
       const int q0h = q0 + 32 * hf_c;
@@ -424,21 +437,57 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
         rows32(q0h, st_c, hf_c, IC<0>{}, false);
     });
   };
-  if (nit > 0) issue(0, IC<0>{});
-  for (int it = 0; it < nit; it += 2) {
+  if (i1 > i0) issue(i0, IC<0>{});
+  for (int it = i0; it < i1; it += 2) {
     step(it, IC<0>{});
-    if (it + 1 < nit) step(it + 1, IC<1>{});
+    if (it + 1 < i1) step(it + 1, IC<1>{});
   }
 
   if (my_k < p.Tk) {
-    bf16* dkr = (bf16*)p.dk + ((size_t)bkv * p.Tk + my_k) * D;
-    bf16* dvr = (bf16*)p.dv + ((size_t)bkv * p.Tk + my_k) * D;
+    if (p.kparts == 1) {
+      bf16* dkr = (bf16*)p.dk + ((size_t)bkv * p.Tk + my_k) * D;
+      bf16* dvr = (bf16*)p.dv + ((size_t)bkv * p.Tk + my_k) * D;
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      store_acc_row<D>(dkr, db, half, dk[db], p.scale);
-      store_acc_row<D>(dvr, db, half, dv[db], 1.f);
+      for (int db = 0; db < ND; ++db) {
+        store_acc_row<D>(dkr, db, half, dk[db], p.scale);
+        store_acc_row<D>(dvr, db, half, dv[db], 1.f);
+      }
+    } else {
+      const size_t row = ((size_t)part * nbkv + bkv) * p.Tk + my_k;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        store_acc_row_f32<D>(p.part_dk + row * D, db, half, dk[db]);
+        store_acc_row_f32<D>(p.part_dv + row * D, db, half, dv[db]);
+      }
     }
   }
+}
+
+// dK = scale * sum of the parts, dV = sum of the parts, in part order; each
+// thread handles 8 consecutive head dimensions of one key row.
+template <int D>
+__global__ void __launch_bounds__(256) bwd_dkdv_merge_kernel(const BwdParams p) {
+  const size_t n8 = (size_t)p.B * p.Hkv * p.Tk * (D / 8);
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const size_t plane = (size_t)p.B * p.Hkv * p.Tk * D;   // floats per part
+  f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+  for (int q = 0; q < p.kparts; ++q) {
+    const f32x4* ks = (const f32x4*)(p.part_dk + q * plane) + 2 * i;
+    const f32x4* vs = (const f32x4*)(p.part_dv + q * plane) + 2 * i;
+    k0 += ks[0];
+    k1 += ks[1];
+    v0 += vs[0];
+    v1 += vs[1];
+  }
+  // 8-byte stores, as the kernels that write dK and dV directly.
+  const float s = p.scale;
+  bf16x4* dk = (bf16x4*)p.dk + 2 * i;
+  bf16x4* dv = (bf16x4*)p.dv + 2 * i;
+  dk[0] = __builtin_shufflevector(to_bf16x2(k0[0] * s, k0[1] * s), to_bf16x2(k0[2] * s, k0[3] * s), 0, 1, 2, 3);
+  dk[1] = __builtin_shufflevector(to_bf16x2(k1[0] * s, k1[1] * s), to_bf16x2(k1[2] * s, k1[3] * s), 0, 1, 2, 3);
+  dv[0] = __builtin_shufflevector(to_bf16x2(v0[0], v0[1]), to_bf16x2(v0[2], v0[3]), 0, 1, 2, 3);
+  dv[1] = __builtin_shufflevector(to_bf16x2(v1[0], v1[1]), to_bf16x2(v1[2], v1[3]), 0, 1, 2, 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -651,13 +700,25 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
   }
   if (p.Tk > 0) {
     const int nkb = (p.Tk + kKeysPerWg - 1) / kKeysPerWg;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nkb * p.B * p.Hkv),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)nkb * p.B * p.Hkv * p.kparts),
                        dim3(kDkdvThreads), 0, stream, p);
+    if (p.kparts > 1) {
+      const size_t n8 = (size_t)p.B * p.Hkv * p.Tk * (D / 8);
+      hipLaunchKernelGGL(bwd_dkdv_merge_kernel<D>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0,
+                         stream, p);
+    }
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int bwd_key_parts(int B, int Hkv, int Tk, bool causal) {
+  // A causal key block's work falls with its position, and with under two
+  // workgroups per compute unit the first blocks set the kernel time.
+  const long long wgs = (long long)B * Hkv * ((Tk + kKeysPerWg - 1) / kKeysPerWg);
+  return causal && wgs < 2LL * compute_units() ? 2 : 1;
+}
 
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream) {
   if (d == 64) return causal ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);

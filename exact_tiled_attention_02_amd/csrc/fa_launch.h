@@ -71,6 +71,13 @@ struct BwdParams {
   int g;             // Hq / Hkv
   float c;           // scale * log2(e) (signed)
   float scale;
+  // Small causal grids: each key block's (query head, query tile) items are
+  // split into kparts contiguous parts, one workgroup each, which write fp32
+  // partial dK and dV [kparts, B*Hkv, Tk, d] that a merge kernel sums in
+  // part order.  kparts = 1: dK and dV are written directly.
+  int kparts;
+  float* part_dk;
+  float* part_dv;
 };
 
 // Rows of each (batch, head) plane of the backward workspace are padded to a
@@ -80,6 +87,9 @@ constexpr int kBwdRowPad = 256;
 // Compute units of the current device (cached per device; 256 if the query
 // fails).
 int compute_units();
+
+// Item parts per dK/dV key block for a backward call (see BwdParams::kparts).
+int bwd_key_parts(int B, int Hkv, int Tk, bool causal);
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int d, bool causal, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int d, bool causal, hipStream_t stream);
