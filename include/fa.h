@@ -156,9 +156,13 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* qscale,
  * order).
  *
  * Workspace: D_i and lse_i * log2(e) per query row (2 * B * Hq * Tqp fp32,
- * Tqp = Tq rounded up to a multiple of 256) in the library-owned buffer of
- * (device, stream) that fa_decode also uses, grown on demand with
- * stream-ordered allocation; fa_release_workspace() frees it.
+ * Tqp = Tq rounded up to a multiple of 256) and, for causal calls with
+ * fewer than two dK/dV workgroups (128 keys each) per compute unit, fp32
+ * partial dK and dV of two halves of every key block's query work
+ * (2 * 2 * B * Hkv * Tk * d fp32), summed in a fixed order by a merge
+ * kernel.  It lives in the library-owned buffer of (device, stream) that
+ * fa_decode also uses, grown on demand with stream-ordered allocation;
+ * fa_release_workspace() frees it.
  * B == 0, Hq == 0 or Tq == Tk == 0 is a valid empty call.  Tq == 0 gives
  * dk = dv = 0 (q, o, lse, dout and dq may then be NULL); Tk == 0 gives
  * dq = 0 (k, v, dk and dv may then be NULL).  Errors: FA_ERR_NULL,
