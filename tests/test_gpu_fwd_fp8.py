@@ -129,3 +129,26 @@ def test_fp8_gpt2_shape_sampled():
         Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
         check_bounded(O[sl], Or, fp8_fwd_error_bound(q, k, v, causal=True, scale=w.scale))
         check("lse", L[sl], Lr, BF16_LSE_TOL)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 32, 8, 4096, 128),   # 512 paired workgroups: light/heavy wavefront pairs
+    (1, 12, 12, 4096, 64),   # 384 paired workgroups, d = 64: key split
+], ids=lambda s: "x".join(map(str, s)))
+def test_fp8_small_causal_grids_sampled_heads(shape):
+    """Causal grids under four workgroups per compute unit take either the
+    key split or light/heavy wavefront pairs, depending on the grid size:
+    full launch, two query heads checked in full against the bound."""
+    B, Hq, Hkv, T, d = shape
+    w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=T, Tk=T, d=d, causal=True, seed=45)
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    say("fa_fwd_fp8 small causal grid", shape)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
+    g = Hq // Hkv
+    for h in (0, Hq - 1):
+        kv = h // g
+        sq, skv = (slice(0, 1), slice(h, h + 1)), (slice(0, 1), slice(kv, kv + 1))
+        q, k, v = oracle.fp8_attention_inputs(q8[sq], k8[skv], v8[skv], qs[sq], ks[skv], vs[skv])
+        Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
+        check_bounded(O[sq], Or, fp8_fwd_error_bound(q, k, v, causal=True, scale=w.scale))
+        check("lse", L[sq], Lr, BF16_LSE_TOL)
