@@ -357,8 +357,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the kernels work on one GPU's share; see DESIGN.md for how it would shard).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(its kernels compute one GPU's share of a sharded job).",
               file=sys.stderr)
         sys.exit(2)
 
