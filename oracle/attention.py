@@ -225,75 +225,100 @@ def attention_backward(q, k, v, do, *, causal: bool, scale: float, align: str = 
 # The online (tiled) fold -- a second, independent route to the same result
 # --------------------------------------------------------------------------
 
+class _RowState:
+    """Running statistics of a set of query rows while key blocks are folded
+    in one at a time: the largest score seen so far (mx), the sum of
+    exp(score - mx) over the keys seen (den) and the exp-weighted sum of
+    their value rows (num), all relative to the same mx.
+
+    Absorbing a block is the rescale rule of [FUSED07] section "Online
+    softmax: вывод" applied to a block instead of a single score (the
+    element form is ``online_weighted_sum``): the new maximum is taken over
+    the old one and the block's scores, the old sums are brought to it by
+    the factor exp(old - new) and the block's own terms are added.
+    """
+
+    def __init__(self, rows: int, width: int):
+        self.mx = np.full(rows, _NEG_INF)
+        self.den = np.zeros(rows)
+        self.num = np.zeros((rows, width))
+
+    def absorb(self, scores: np.ndarray, values: np.ndarray) -> None:
+        """Fold one key block in: scores [rows, keys] (hidden keys at -inf),
+        values [keys, width]."""
+        grown = np.fmax(self.mx, scores.max(axis=1, initial=_NEG_INF))
+        # Rows that still have no visible key keep every sum at zero; any
+        # finite anchor works for them, 0 avoids (-inf) - (-inf).
+        anchor = np.where(np.isinf(grown), 0.0, grown)
+        keep = np.exp(self.mx - anchor)            # exp(old max - new max)
+        w = np.exp(scores - anchor[:, None])       # exp(score - new max)
+        self.den = keep * self.den + w.sum(axis=1)
+        self.num = keep[:, None] * self.num + w @ values
+        self.mx = grown
+
+    def result(self) -> Tuple[np.ndarray, np.ndarray]:
+        """(num / den, mx + log den); rows that saw no key give (0, -inf)."""
+        seen = self.den > 0
+        out = np.zeros_like(self.num)
+        lse = np.full(self.mx.shape, _NEG_INF)
+        out[seen] = self.num[seen] / self.den[seen, None]
+        lse[seen] = self.mx[seen] + np.log(self.den[seen])
+        return out, lse
+
+
+def _key_blocks_needed(first_row: int, last_row: int, Tk: int, Bc: int, causal: bool,
+                       off: int) -> int:
+    """Key blocks of width Bc a query block must visit: all of them, or under
+    the causal mask only those that begin at or before the last row's
+    furthest visible key ([FUSED07] section "FlashAttention-2", change 3:
+    later blocks lie wholly above the diagonal)."""
+    reach = Tk if not causal else max(0, min(Tk, last_row + off + 1))
+    return -(-reach // Bc)
+
+
 def online_fold_attention(q, k, v, *, causal: bool, scale: float, Br: int = 64,
                           Bc: int = 64, count: bool = False, align: str = "top_left"):
-    """FlashAttention forward in fp64, FA-2 loop order.
+    """Exact attention reached the tiled way, in fp64 (a second route to the
+    definition that ``softmax_attention`` writes out).
 
-    Follows [LESSON] section "Прямой проход FlashAttention" and [FUSED07]
-    section "Online softmax: вывод": for each block of Br query rows keep a
-    running max m, a running sum l and an unnormalised accumulator A; for
-    each block of Bc keys
-
-        S  = scale * Q_i K_j^T           (masked entries -> -inf, before max)
-        m' = max(m, rowmax S)
-        P  = exp(S - m')
-        l  = l * exp(m - m') + rowsum P
-        A  = A * exp(m - m') + P V_j,    m = m'
-
-    and after the last block O = A / l (one division per row) and
-    lse = m + log l.  Under the causal mask key blocks that start after the
-    last row of the query block are skipped ([FUSED07] section
-    "FlashAttention-2", change 3).  Returns (O, lse) or, with ``count``,
-    (O, lse, visited_block_pairs).
+    The query rows of every (batch, head) are cut into blocks of Br; each
+    block keeps a ``_RowState`` and folds the key/value sequence into it in
+    blocks of Bc, in order, with the block's masked scores at -inf before
+    any maximum is taken.  One division per row at the end gives O and
+    lse = max + log(sum) ([LESSON] sections "Прямой проход FlashAttention"
+    and "Обратный проход": L = m + log l).  Key blocks that lie wholly
+    above the causal diagonal are never visited.  Returns (O, lse) or,
+    with ``count``, (O, lse, number of (query block, key block) pairs
+    visited).
     """
-    q = as_f64(q)
-    k = as_f64(k)
-    v = as_f64(v)
-    B, Hq, Tq, d = q.shape
-    Hkv, Tk = k.shape[1], k.shape[2]
-    g = Hq // Hkv
-    dv = v.shape[3]
+    qs, ks, vs = as_f64(q), as_f64(k), as_f64(v)
+    B, Hq, Tq, _ = qs.shape
+    Hkv, Tk, width = ks.shape[1], ks.shape[2], vs.shape[3]
+    group = Hq // Hkv
     off = causal_offset(Tq, Tk, align)
-    O = np.zeros((B, Hq, Tq, dv))
-    L = np.full((B, Hq, Tq), _NEG_INF)
-    pairs = 0
-    for b in range(B):
-        for h in range(Hq):
-            K = k[b, h // g]
-            V = v[b, h // g]
-            for i0 in range(0, Tq, Br):
-                Qi = q[b, h, i0:i0 + Br]
-                n = Qi.shape[0]
-                i_last = i0 + n - 1
-                m = np.full(n, _NEG_INF)
-                l = np.zeros(n)
-                A = np.zeros((n, dv))
-                for j0 in range(0, Tk, Bc):
-                    if causal and j0 > i_last + off:
-                        break
-                    pairs += 1
-                    Kj = K[j0:j0 + Bc]
-                    Vj = V[j0:j0 + Bc]
-                    S = (Qi @ Kj.T) * scale
-                    if causal:
-                        rows = np.arange(i0, i0 + n)[:, None]
-                        cols = np.arange(j0, j0 + Kj.shape[0])[None, :]
-                        S = np.where(cols > rows + off, _NEG_INF, S)
-                    m_new = np.maximum(m, S.max(axis=1))
-                    # A row that has seen no visible key keeps m' = -inf; its
-                    # sums stay zero (exp of -inf), so subtract 0 instead.
-                    ref = np.where(np.isfinite(m_new), m_new, 0.0)
-                    corr = np.exp(m - ref)
-                    P = np.exp(S - ref[:, None])
-                    l = l * corr + P.sum(axis=1)
-                    A = A * corr[:, None] + P @ Vj
-                    m = m_new
-                ok = l > 0
-                O[b, h, i0:i0 + n][ok] = A[ok] / l[ok, None]
-                L[b, h, i0:i0 + n][ok] = m[ok] + np.log(l[ok])
+    out = np.zeros((B, Hq, Tq, width))
+    lse = np.full((B, Hq, Tq), _NEG_INF)
+    visited = 0
+    key_pos = np.arange(Tk)
+    for b, h in ((b, h) for b in range(B) for h in range(Hq)):
+        keys, vals = ks[b, h // group], vs[b, h // group]
+        for r0 in range(0, Tq, Br):
+            r1 = min(Tq, r0 + Br)
+            row_pos = np.arange(r0, r1)
+            state = _RowState(r1 - r0, width)
+            nkb = _key_blocks_needed(r0, r1 - 1, Tk, Bc, causal, off)
+            for kb in range(nkb):
+                cols = key_pos[kb * Bc:(kb + 1) * Bc]
+                sc = scale * (qs[b, h, r0:r1] @ keys[cols].T)
+                if causal:
+                    hidden = cols[None, :] - row_pos[:, None] > off
+                    sc[hidden] = _NEG_INF
+                state.absorb(sc, vals[cols])
+            visited += nkb
+            out[b, h, r0:r1], lse[b, h, r0:r1] = state.result()
     if count:
-        return O, L, pairs
-    return O, L
+        return out, lse, visited
+    return out, lse
 
 
 def causal_block_pairs(Tq: int, Tk: int, Br: int, Bc: int, causal: bool) -> int:
