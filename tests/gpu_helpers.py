@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: move bf16 bit patterns to and from the
 device, and compare the HIP results with the oracle."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -41,6 +43,53 @@ def check(name, got, want, tol):
     e = max_err(got, want)
     print(f"  {name}: max|err| = {e:.3e} (bar {tol:.1e})", flush=True)
     assert e <= tol, f"{name}: {e} > {tol}"
+
+
+def pool_workers() -> int:
+    """Threads for oracle work: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def head_map(fn, items):
+    """fn over items on a thread pool, one-threaded BLAS inside each call (the
+    oracle's array operations release the interpreter lock)."""
+    from threadpoolctl import threadpool_limits
+    items = list(items)
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(pool_workers()) as ex:
+            return list(ex.map(fn, items))
+
+
+def check_every_element(O, L, q, k, v, *, causal, scale, align="top_left",
+                        o_tol=None, lse_tol=None):
+    """Compare every element of O [B,Hq,Tq,d] and L [B,Hq,Tq] with the oracle,
+    one (batch, head) per task.  Returns (max |O err|, max |lse err|)."""
+    import oracle
+    o_tol = BF16_O_TOL if o_tol is None else o_tol
+    lse_tol = BF16_LSE_TOL if lse_tol is None else lse_tol
+    B, Hq = q.shape[:2]
+    g = Hq // k.shape[1]
+
+    def one(bh):
+        b, h = bh
+        kv = h // g
+        Or, Lr = oracle.softmax_attention(q[b:b + 1, h:h + 1], k[b:b + 1, kv:kv + 1],
+                                          v[b:b + 1, kv:kv + 1], causal=causal, scale=scale,
+                                          align=align)
+        return max_err(O[b, h], Or[0, 0]), max_err(L[b, h], Lr[0, 0])
+
+    errs = head_map(one, [(b, h) for b in range(B) for h in range(Hq)])
+    eo = max(e[0] for e in errs) if errs else 0.0
+    el = max(e[1] for e in errs) if errs else 0.0
+    print(f"  O: max|err| = {eo:.3e} (bar {o_tol:.1e}) over {B * Hq} heads", flush=True)
+    print(f"  lse: max|err| = {el:.3e} (bar {lse_tol:.1e})", flush=True)
+    assert eo <= o_tol, f"O: {eo} > {o_tol}"
+    assert el <= lse_tol, f"lse: {el} > {lse_tol}"
+    return eo, el
 
 
 def max_err(a, b):
@@ -177,3 +226,92 @@ def fp8_fwd_error_bound(q, k, v, *, causal, scale, causal_off=0, safety=1.25):
             bound[b, h] = (dP @ np.abs(v[b, kh])) / lsafe
             O[b, h] = (P @ v[b, kh]) / lsafe
     return safety * (bound + 2.0 ** -8 * np.abs(O)) + 1e-6
+
+
+def fp8_fwd_error_bound_rows(q, k, v, rows, *, causal, scale, causal_off=0, safety=1.25):
+    """fp8_fwd_error_bound for selected query rows of one head: q [n, d] the
+    dequantised rows, rows [n] their positions, k, v [Tk, d] the dequantised
+    keys and values of the head's kv head."""
+    rows = np.asarray(rows)
+    Tk = k.shape[0]
+    vis = (np.arange(Tk)[None, :] <= rows[:, None] + causal_off) if causal else \
+        np.ones((len(rows), Tk), bool)
+    s = np.where(vis, scale * (q @ k.T), -np.inf)
+    m = np.max(s, axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    P = np.where(vis, np.exp(s - m), 0.0)
+    l = P.sum(axis=1, keepdims=True)
+    lsafe = np.where(l > 0, l, 1.0)
+    dP = np.where(vis, np.maximum(E4M3_U * P, E4M3_FLOOR), 0.0)
+    bound = (dP @ np.abs(v)) / lsafe
+    O = (P @ v) / lsafe
+    return safety * (bound + 2.0 ** -8 * np.abs(O)) + 1e-6
+
+
+def check_fp8_every_head(O, L, q8, k8, v8, qs, ks, vs, *, causal, scale, align="top_left",
+                         heads=None):
+    """Every element of the listed (batch, query head) pairs of an 8-bit
+    forward (all pairs by default) against the oracle on the dequantised
+    inputs: O within fp8_fwd_error_bound, lse within BF16_LSE_TOL.  One pair
+    per thread-pool task.  Returns (worst err/bound, max |lse err|)."""
+    import oracle
+    B, Hq, Tq = q8.shape[:3]
+    Tk = k8.shape[2]
+    g = Hq // k8.shape[1]
+    off = oracle.causal_offset(Tq, Tk, align)
+    heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
+
+    def one(bh):
+        b, h = bh
+        kv = h // g
+        sq, skv = (slice(b, b + 1), slice(h, h + 1)), (slice(b, b + 1), slice(kv, kv + 1))
+        q, k, v = oracle.fp8_attention_inputs(q8[sq], k8[skv], v8[skv], qs[sq], ks[skv], vs[skv])
+        Or, Lr = oracle.softmax_attention(q, k, v, causal=causal, scale=scale, align=align)
+        bound = fp8_fwd_error_bound(q, k, v, causal=causal, scale=scale, causal_off=off)
+        got = O[sq]
+        ok = bool(np.all(np.isfinite(got)))
+        ratio = float(np.max(np.abs(got - Or) / bound)) if got.size else 0.0
+        return ok, ratio, max_err(L[sq], Lr)
+
+    res = head_map(one, heads)
+    finite = all(r[0] for r in res)
+    ratio = max((r[1] for r in res), default=0.0)
+    el = max((r[2] for r in res), default=0.0)
+    print(f"  O: max err/bound = {ratio:.3f} over {len(heads)} heads", flush=True)
+    print(f"  lse: max|err| = {el:.3e} (bar {BF16_LSE_TOL:.1e})", flush=True)
+    assert finite, "non-finite output"
+    assert ratio <= 1.0, f"O error exceeds its bound (ratio {ratio:.3f})"
+    assert el <= BF16_LSE_TOL, f"lse: {el} > {BF16_LSE_TOL}"
+    return ratio, el
+
+
+def lse_error_bound(q, k, L, *, causal, scale, causal_off=0, safety=1.25):
+    """Bound on |lse_kernel - lse_exact| per query row for bf16 inputs.
+
+    q, k: fp64 values of the bf16 inputs [B,Hq,Tq,d], [B,Hkv,Tk,d]; L the
+    exact lse.  A product of two bf16 values is exact in fp32 and the kernel
+    sums the d products of a score in fp32, so each computed score is off
+    by at most g_d sum_t |q_it k_jt| (g_d = d 2^-24 / (1 - d 2^-24)); the
+    log-sum-exp moves by at most |scale| times the largest score error.  The
+    rest is fp32 rounding of O(1) relative size: of c = |scale| log2(e), of
+    the exponent arguments, of the n-term row sum, of log2 and of the final
+    conversion to a natural log, together at most
+    (8 |L_i| + n + 16) 2^-24.  Times `safety`.  Rows with no visible key
+    (L = -inf) get 0."""
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    gd = d * F32_U / (1 - d * F32_U)
+    n = max(Tk, 1)
+    out = np.zeros((B, Hq, Tq))
+    i_idx = np.arange(Tq)[:, None]
+    j_idx = np.arange(Tk)[None, :]
+    vis = (j_idx <= i_idx + causal_off) if causal else np.ones((Tq, Tk), bool)
+    for b in range(B):
+        for h in range(Hq):
+            mag = np.abs(q[b, h]) @ np.abs(k[b, h // g]).T
+            worst = np.max(np.where(vis, mag, 0.0), axis=1) if Tk else np.zeros(Tq)
+            Lf = np.where(np.isfinite(L[b, h]), np.abs(L[b, h]), 0.0)
+            e = abs(scale) * gd * worst + (8 * Lf + n + 16) * F32_U
+            out[b, h] = np.where(np.isfinite(L[b, h]), safety * e, 0.0)
+    return out

@@ -12,7 +12,8 @@ import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import BF16_LSE_TOL, check, fp8_fwd_error_bound, host_bf16_as_f64, host_f64, say
+from gpu_helpers import (BF16_LSE_TOL, check, check_fp8_every_head, fp8_fwd_error_bound,
+                         fp8_fwd_error_bound_rows, host_bf16_as_f64, host_f64, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +81,10 @@ SMALL = [
     (1, 8, 1, 70, 70, 128, True),
     (1, 2, 2, 128, 128, 128, False),
     (1, 1, 1, 383, 383, 128, True),
+    (1, 8, 2, 300, 300, 128, False),   # non-causal, g = 4
+    (1, 8, 4, 257, 190, 64, False),    # non-causal, g = 2, Tq != Tk
+    (2, 8, 2, 130, 333, 64, False),    # non-causal, g = 4, d = 64
+    (1, 4, 2, 65, 129, 128, False),    # non-causal, g = 2, d = 128
 ]
 
 
@@ -116,39 +121,89 @@ def test_fp8_qwen3_shape_full():
     parity(w)
 
 
-def test_fp8_gpt2_shape_sampled():
-    """B=8, H=12, T=4096, d=64 causal in 8 bits: full launch; two (batch,
-    head) pairs checked in full."""
+def test_fp8_gpt2_shape_every_element():
+    """B=8, H=12, T=4096, d=64 causal in 8 bits: every element of every
+    (batch, head) pair against the bound."""
     w = inputs.Prefill("gpt2 fp8", B=8, Hq=12, Hkv=12, Tq=4096, Tk=4096, d=64, causal=True)
     q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
     say("fa_fwd_fp8", w.name)
     O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
-    for b, h in ((0, 0), (7, 11)):
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        q, k, v = oracle.fp8_attention_inputs(q8[sl], k8[sl], v8[sl], qs[sl], ks[sl], vs[sl])
-        Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
-        check_bounded(O[sl], Or, fp8_fwd_error_bound(q, k, v, causal=True, scale=w.scale))
-        check("lse", L[sl], Lr, BF16_LSE_TOL)
+    check_fp8_every_head(O, L, q8, k8, v8, qs, ks, vs, causal=True, scale=w.scale)
 
 
 @pytest.mark.parametrize("shape", [
     (1, 32, 8, 4096, 128),   # 512 paired workgroups: light/heavy wavefront pairs
     (1, 12, 12, 4096, 64),   # 384 paired workgroups, d = 64: key split
 ], ids=lambda s: "x".join(map(str, s)))
-def test_fp8_small_causal_grids_sampled_heads(shape):
+def test_fp8_small_causal_grids_every_head(shape):
     """Causal grids under four workgroups per compute unit take either the
     key split or light/heavy wavefront pairs, depending on the grid size:
-    full launch, two query heads checked in full against the bound."""
+    full launch, every element of every head against the bound."""
     B, Hq, Hkv, T, d = shape
     w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=T, Tk=T, d=d, causal=True, seed=45)
     q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
     say("fa_fwd_fp8 small causal grid", shape)
     O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
-    g = Hq // Hkv
-    for h in (0, Hq - 1):
-        kv = h // g
+    check_fp8_every_head(O, L, q8, k8, v8, qs, ks, vs, causal=True, scale=w.scale)
+
+
+# The three causal schedules (heaviest-first, light/heavy wavefront pairs,
+# key split) for each head dimension and number of query heads per
+# workgroup, as for the bf16 kernel: T = 2048, every element of every head.
+GRID_SCHEMES = [
+    # scheme, B, Hq, Hkv, d  (workgroups: heaviest-first 1024, pairs 768, key split 256)
+    ("heaviest-first", 8, 16, 16, 64), ("heaviest-first", 8, 16, 16, 128),
+    ("heaviest-first", 8, 16, 8, 64), ("heaviest-first", 8, 16, 8, 128),
+    ("heaviest-first", 4, 32, 8, 64), ("heaviest-first", 4, 32, 8, 128),
+    ("pairs", 6, 16, 16, 64), ("pairs", 6, 16, 16, 128),
+    ("pairs", 6, 16, 8, 64), ("pairs", 6, 16, 8, 128),
+    ("pairs", 3, 32, 8, 64), ("pairs", 3, 32, 8, 128),
+    ("key-split", 2, 16, 16, 64), ("key-split", 2, 16, 16, 128),
+    ("key-split", 2, 16, 8, 64), ("key-split", 2, 16, 8, 128),
+    ("key-split", 1, 32, 8, 64), ("key-split", 1, 32, 8, 128),
+]
+
+
+@pytest.mark.parametrize("case", GRID_SCHEMES, ids=lambda c: "-".join(map(str, c)))
+def test_fp8_causal_grid_schemes_every_element(case):
+    _, B, Hq, Hkv, d = case
+    w = inputs.Prefill("t", B=B, Hq=Hq, Hkv=Hkv, Tq=2048, Tk=2048, d=d, causal=True, q_mult=2.0,
+                       seed=46)
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    say("fa_fwd_fp8 causal grid", case)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
+    check_fp8_every_head(O, L, q8, k8, v8, qs, ks, vs, causal=True, scale=w.scale)
+
+
+def test_fp8_noncausal_gqa_large_grid_every_element():
+    w = inputs.Prefill("t", B=2, Hq=32, Hkv=8, Tq=1500, Tk=2100, d=128, causal=False, seed=47)
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    say("fa_fwd_fp8 non-causal GQA", w)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 0, w.scale)
+    check_fp8_every_head(O, L, q8, k8, v8, qs, ks, vs, causal=False, scale=w.scale)
+
+
+def test_fp8_llama3_shape_sampled_rows():
+    """The Llama-3-8B 32K GQA shape in 8 bits (Hq=32, Hkv=8, T=32768, d=128;
+    4096 workgroups, heaviest query tile first, four query heads per
+    workgroup): full launch; the first and last 128 rows and 256 random rows
+    of six heads against the oracle and the derived bound."""
+    w = inputs.LLAMA3_8B_LONG_FP8
+    q8, k8, v8, qs, ks, vs = inputs.prefill_inputs_fp8(w)
+    say("fa_fwd_fp8", w.name)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1, w.scale)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    rng = np.random.default_rng(48)
+    T = w.Tq
+    for h in (0, 5, 13, 18, 27, 31):
+        rows = sorted(set(range(128)) | set(range(T - 128, T)) |
+                      set(rng.choice(T, size=256, replace=False).tolist()))
+        kv = h // (w.Hq // w.Hkv)
         sq, skv = (slice(0, 1), slice(h, h + 1)), (slice(0, 1), slice(kv, kv + 1))
         q, k, v = oracle.fp8_attention_inputs(q8[sq], k8[skv], v8[skv], qs[sq], ks[skv], vs[skv])
-        Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=w.scale)
-        check_bounded(O[sq], Or, fp8_fwd_error_bound(q, k, v, causal=True, scale=w.scale))
-        check("lse", L[sq], Lr, BF16_LSE_TOL)
+        Or, Lr = oracle.softmax_attention_rows(q, k, v, causal=True, scale=w.scale, b=0, h=0,
+                                               rows=rows)
+        bound = fp8_fwd_error_bound_rows(q[0, 0, rows], k[0, 0], v[0, 0], rows, causal=True,
+                                         scale=w.scale)
+        check_bounded(O[0, h, rows], Or, bound)
+        check("lse", L[0, h, rows], Lr, BF16_LSE_TOL)
