@@ -26,23 +26,23 @@ int map_err(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 // A library-owned device buffer of at least `need` bytes for calls on
 // `stream` of the current device: grown (by a quarter more than asked) with
-// stream-ordered allocation, kept for the next call.
+// stream-ordered allocation, kept for the next call.  The larger buffer is
+// allocated before the old one is released, so a failed allocation returns
+// FA_ERR_ALLOC with nothing enqueued and the old buffer still held.
 int workspace(hipStream_t stream, size_t need, char** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_DEVICE;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   Workspace& w = g_ws[std::make_pair(dev, stream)];
   if (w.bytes < need) {
-    if (w.ptr != nullptr) {
-      if (hipFreeAsync(w.ptr, stream) != hipSuccess) return FA_ERR_ALLOC;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
     const size_t grow = need + need / 4;
-    if (hipMallocAsync(&w.ptr, grow, stream) != hipSuccess) {
-      w.ptr = nullptr;
-      return FA_ERR_ALLOC;
-    }
+    void* fresh = nullptr;
+    if (hipMallocAsync(&fresh, grow, stream) != hipSuccess) return FA_ERR_ALLOC;
+    // The old buffer is released after every earlier call on this stream
+    // (stream order).  Should the release be refused, the buffer is left
+    // to the process's end rather than failing this call.
+    if (w.ptr != nullptr) (void)hipFreeAsync(w.ptr, stream);
+    w.ptr = fresh;
     w.bytes = grow;
   }
   *out = (char*)w.ptr;

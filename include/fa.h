@@ -11,6 +11,9 @@
  *             połączona dekwantyzacja" -- trefon.com notes.
  *   [BOOK5]   "Глава 5. Операторы и среда выполнения" -- AI infra book,
  *             bojieli.github.io.
+ *   [FA3QA]   "Как работает FlashAttention-3 математически?" -- aivaro.ru
+ *             (the Hopper FlashAttention-3 design: FP8 operands with
+ *             higher-precision accumulation, section 6).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -25,8 +28,14 @@
  *    A fault inside a kernel therefore surfaces at the caller's next
  *    synchronisation, not in the return code.
  *  - Return value: FA_OK (0) or one of the fa_status codes below.  Argument
- *    checks happen before any HIP call; on a nonzero return nothing has been
- *    enqueued.
+ *    checks happen before any HIP call, and a workspace is grown before the
+ *    first kernel is launched: after FA_ERR_NULL, FA_ERR_SHAPE,
+ *    FA_ERR_UNSUPPORTED, FA_ERR_ALLOC or FA_ERR_DEVICE nothing has been
+ *    enqueued.  FA_ERR_LAUNCH from an entry point that launches several
+ *    kernels (fa_decode and its 8-bit forms: a range kernel and a merge
+ *    kernel; fa_bwd: up to four kernels) may leave the kernels launched
+ *    before the rejected one enqueued; their results are then incomplete
+ *    and the outputs must not be used.
  *  - Device addresses are not validated beyond non-NULL: passing buffers
  *    smaller than the stated shapes is undefined behaviour.
  */
