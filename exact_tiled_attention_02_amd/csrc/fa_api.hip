@@ -246,9 +246,14 @@ int decode_workgroups_checked(int B, int Hq, int Hkv, int Tk_max, int d, int num
   return decode_workgroups(d, fa::decode_heads_per_workgroup(Hq / Hkv), kv, num_splits);
 }
 
+// fixed_ws == nullptr: the workspace comes from the per-(device, stream)
+// buffer, grown on demand.  Otherwise it is the caller-provided device
+// memory fixed_ws of fixed_cap bytes; a call that needs more returns
+// FA_ERR_SCRATCH before anything is enqueued.
 int decode_impl(const void* q, const void* kcache, const void* vcache, const float* kscale,
                 const float* vscale, const int* seqlens, void* o, int B, int Hq, int Hkv,
-                int Tk_max, int d, int num_splits, int kv, void* stream) {
+                int Tk_max, int d, int num_splits, int kv, void* stream,
+                char* fixed_ws = nullptr, size_t fixed_cap = 0) {
   if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
@@ -270,9 +275,13 @@ int decode_impl(const void* q, const void* kcache, const void* vcache, const flo
   const size_t need = cum_bytes + nparts * (size_t)(d + 2) * sizeof(float);
   hipStream_t hs = (hipStream_t)stream;
 
-  char* ws = nullptr;
-  const int wst = workspace(hs, need, &ws);
-  if (wst != FA_OK) return wst;
+  char* ws = fixed_ws;
+  if (ws == nullptr) {
+    const int wst = workspace(hs, need, &ws);
+    if (wst != FA_OK) return wst;
+  } else if (need > fixed_cap) {
+    return FA_ERR_SCRATCH;
+  }
 
   fa::DecodeParams p{};
   p.q = q;
@@ -297,6 +306,40 @@ int decode_impl(const void* q, const void* kcache, const void* vcache, const flo
   return map_err(fa::launch_decode(p, d, kv, hs));
 }
 
+// Workspace of fa_decode_noalloc: a fixed device array in this library's
+// code object, one copy per device, held until the process ends.  Host code
+// never uses its name as an address (on the host the name is only a stand-in
+// for the symbol): the device address of each device's copy is looked up
+// once, with that device current, and kept per device.  Every slot the merge
+// kernel reads was written earlier in the same call, so nothing in it has to
+// start at zero.
+static __device__ __align__(256) char scratch[FA_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of the current device's scratch copy, or null with *status
+// set (FA_ERR_DEVICE) when the device or the symbol cannot be queried.
+char* scratch_address(int* status) {
+  static std::mutex mu;
+  static char* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *status = FA_ERR_DEVICE;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      *status = FA_ERR_DEVICE;
+      return nullptr;
+    }
+    addr[dev] = (char*)ptr;
+  }
+  *status = FA_OK;
+  return addr[dev];
+}
+
 }  // namespace
 
 int fa_decode_workgroups(int B, int Hq, int Hkv, int Tk_max, int d, int num_splits) {
@@ -315,6 +358,18 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int* 
               int B, int Hq, int Hkv, int Tk_max, int d, int num_splits, void* stream) {
   return decode_impl(q, kcache, vcache, nullptr, nullptr, seqlens, o, B, Hq, Hkv, Tk_max, d,
                      num_splits, fa::kKvBf16, stream);
+}
+
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int* seqlens,
+                      void* o, int B, int Hq, int Hkv, int Tk_max, int d, int num_splits,
+                      void* stream) {
+  if (B < 0 || Hq < 0 || Hkv < 1 || Tk_max < 0 || num_splits < 0) return FA_ERR_SHAPE;
+  if (B == 0 || Hq == 0) return FA_OK;
+  int st = FA_OK;
+  char* ws = scratch_address(&st);
+  if (ws == nullptr) return st;
+  return decode_impl(q, kcache, vcache, nullptr, nullptr, seqlens, o, B, Hq, Hkv, Tk_max, d,
+                     num_splits, fa::kKvBf16, stream, ws, FA_DECODE_SCRATCH_BYTES);
 }
 
 int fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const float* kscale,
@@ -347,6 +402,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALLOC: return "workspace allocation failed";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_DEVICE: return "no usable HIP device";
+    case FA_ERR_SCRATCH: return "workspace exceeds the fixed decode scratch (FA_DECODE_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -1,6 +1,7 @@
 """Python binding of the HIP library ``libfa.so`` (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_decode``, ``fa_decode_workgroups``,
+The functions ``fa_fwd``, ``fa_fwd_f32``, ``fa_fwd_fp8``, ``fa_bwd``, ``fa_decode``,
+``fa_decode_noalloc``, ``fa_decode_workgroups``,
 ``fa_decode_fp8``, ``fa_decode_fp8_workgroups``, ``fa_decode_int8``, ``fa_decode_int8_workgroups``,
 ``fa_read_probe``, ``fa_strerror`` and ``fa_release_workspace`` mirror the C entry points of
 ``include/fa.h`` one to one: pointers may be given as integers or as objects
@@ -25,7 +26,8 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-                4: "FA_ERR_ALLOC", 5: "FA_ERR_LAUNCH", 6: "FA_ERR_DEVICE"}
+                4: "FA_ERR_ALLOC", 5: "FA_ERR_LAUNCH", 6: "FA_ERR_DEVICE", 7: "FA_ERR_SCRATCH"}
+DECODE_SCRATCH_BYTES = 4 << 20   # FA_DECODE_SCRATCH_BYTES of include/fa.h
 STATUS_CODES = {v: k for k, v in STATUS_NAMES.items()}
 
 _lib = None
@@ -59,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa_bwd.restype = I
         lib.fa_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
         lib.fa_decode.restype = I
+        lib.fa_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.fa_decode_noalloc.restype = I
         lib.fa_decode_workgroups.argtypes = [I, I, I, I, I, I]
         lib.fa_decode_workgroups.restype = I
         lib.fa_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P]
@@ -146,6 +150,13 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, d, causal, sca
 def fa_decode(q, kcache, vcache, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits, stream=None) -> None:
     _check(load().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o), B, Hq,
                             Hkv, Tk_max, d, int(num_splits), _stream(stream)), "fa_decode")
+
+
+def fa_decode_noalloc(q, kcache, vcache, seqlens, o, B, Hq, Hkv, Tk_max, d, num_splits,
+                      stream=None) -> None:
+    _check(load().fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(seqlens), _ptr(o), B,
+                                    Hq, Hkv, Tk_max, d, int(num_splits), _stream(stream)),
+           "fa_decode_noalloc")
 
 
 def fa_decode_workgroups(B, Hq, Hkv, Tk_max, d, num_splits) -> int:

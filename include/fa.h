@@ -55,7 +55,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED = 3,  /* head dimension other than 64 or 128             */
   FA_ERR_ALLOC = 4,        /* a library workspace could not be allocated     */
   FA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch        */
-  FA_ERR_DEVICE = 6        /* no usable HIP device / runtime error            */
+  FA_ERR_DEVICE = 6,       /* no usable HIP device / runtime error            */
+  FA_ERR_SCRATCH = 7       /* fa_decode_noalloc: workspace over the fixed size */
 } fa_status;
 
 /*
@@ -226,6 +227,32 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int* seqlens,
               void* o, int B, int Hq, int Hkv, int Tk_max, int d, int num_splits,
               void* stream);
+
+/* Bytes of the fixed per-device workspace of fa_decode_noalloc. */
+#define FA_DECODE_SCRATCH_BYTES (4u << 20)
+
+/*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, serving loops and harnesses
+ * that forbid allocation.  Same arguments, operation, result (bitwise equal
+ * to fa_decode with the same num_splits) and errors, but the workspace
+ * (prefix sums and partials, sized as for fa_decode) is a fixed array of
+ * FA_DECODE_SCRATCH_BYTES bytes inside the library, one per device, which
+ * the device holds from the library's load until the process ends.  Nothing
+ * is allocated or freed (no hipMalloc, hipFree or allocating library
+ * routine); the first call on a device looks up the array's device address
+ * once.  A call whose workspace would exceed the array returns
+ * FA_ERR_SCRATCH with nothing enqueued (at d = 128 with four query heads
+ * per workgroup a slot takes 2080 bytes, so about 2000 slots fit: e.g. the
+ * 512 automatic key ranges plus up to about 1500 (sequence, kv-head group)
+ * segments).  All calls on one device share the
+ * array: calls that can overlap in time on one device (different streams,
+ * several host threads) race and give wrong results; the caller orders
+ * them.  fa_release_workspace() does not touch it.
+ */
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int* seqlens,
+                      void* o, int B, int Hq, int Hkv, int Tk_max, int d, int num_splits,
+                      void* stream);
 
 /* The number of key ranges (workgroups) fa_decode uses for a request, after
  * the 0 = automatic choice (which needs a current HIP device) and the cap,
