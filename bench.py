@@ -4,19 +4,23 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step is one fa_fwd call (the whole prefill path: Q tile load, K/V tile
-streaming, QK^T, masking, online softmax, PV, finalise) over the GPT-2-small
-shaped causal MHA workload (B=8, H=12, T=4096, d=64, bf16).  `value` is its
-attention TFLOP/s (4*B*H*T*T*d/2 per call) over the wall-clock of K
+streaming, QK^T, masking, online softmax, PV, finalise) over the
+Llama-3-8B-shaped long-context causal GQA workload (B=1, Hq=32, Hkv=8,
+T=32768, d=128, bf16), the largest of the prefill workloads.  `value` is its
+attention TFLOP/s (4*B*Hq*T*T*d/2 per call) over the wall-clock of K
 back-to-back steps, inputs resident in HBM.  The same JSON line carries:
 
-  roofline      achieved FLOP/s of the forward kernel (average launch
-                duration from HIP events on the launch stream) against the
-                dense bf16 matrix-core peak;
-  also          the other workloads measured the same way: Qwen3-0.6B GQA
-                prefill, Llama-3-8B long-context GQA prefill (TFLOP/s) and
-                split-KV decode over a 16-sequence cache (HBM GB/s);
+  roofline      achieved FLOP/s of the forward kernel (mean launch duration
+                from HIP events recorded on the launch stream around every
+                launch; median and min beside it) against the dense bf16
+                matrix-core peak;
+  also          the other workloads measured the same way, each with its own
+                roofline block: Qwen3-0.6B GQA prefill and GPT-2-small MHA
+                prefill (TFLOP/s), chunked prefill, 8-bit prefill, the
+                backward pass, and split-KV decode over a 16-sequence cache
+                (HBM GB/s) with a sweep of the split count;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the
-                headline workload on this host.
+                headline workload (whole heads, one per host thread).
 
 Only rank 0 at one GPU is supported; more GPUs exit with a message.
 """
@@ -109,24 +113,27 @@ def dev_normal(torch, shape, gen, mult=1.0):
     return x.to(torch.bfloat16)
 
 
-def time_calls(torch, launch, steps: int, warmup: int):
+def time_calls(torch, launch, steps: int, warmup: int) -> dict:
     """Run `launch` warmup times, then `steps` times back to back, bracketed
-    by device synchronisation.  Returns (wall seconds per call, event ms per
-    call): HIP events recorded on the launch stream before the first and
-    after the last timed call give the average launch duration."""
+    by device synchronisation.  HIP events recorded on the launch stream
+    (torch's current stream, which every launch here uses) before each timed
+    call and after the last give each call's duration.  Returns wall
+    seconds per call and the mean, median and min event duration in ms."""
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(steps):
+    for i in range(steps):
+        events[i].record()
         launch()
-    end.record()
+    events[steps].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    return wall, start.elapsed_time(end) / steps
+    per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
+    mid = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return {"wall_s": wall, "mean_ms": events[0].elapsed_time(events[steps]) / steps,
+            "median_ms": mid, "min_ms": per[0]}
 
 
 def prefill_case(torch, fa, w, steps, warmup, seed=0):
@@ -151,9 +158,9 @@ def prefill_case(torch, fa, w, steps, warmup, seed=0):
         o = torch.empty((w.B, w.Hq, w.Tq, w.d), dtype=torch.bfloat16, device="cuda")
         launch = fa.prepared("fa_fwd_fp8", q, k, v, qs, ks, vs, o, lse, w.B, w.Hq, w.Hkv, w.Tq,
                              w.Tk, w.d, w.causal_mode, w.scale, stream=stream)
-        wall, ev_ms = time_calls(torch, launch, steps, warmup)
+        t = time_calls(torch, launch, steps, warmup)
         del q, k, v, qs, ks, vs, o, lse
-        return wall, ev_ms
+        return t
     q = dev_normal(torch, (w.B, w.Hq, w.Tq, w.d), gen, w.q_mult)
     k = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
     v = dev_normal(torch, (w.B, w.Hkv, w.Tk, w.d), gen)
@@ -161,9 +168,9 @@ def prefill_case(torch, fa, w, steps, warmup, seed=0):
 
     launch = fa.prepared("fa_fwd", q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.d,
                          w.causal_mode, w.scale, stream=stream)
-    wall, ev_ms = time_calls(torch, launch, steps, warmup)
+    t = time_calls(torch, launch, steps, warmup)
     del q, k, v, o, lse
-    return wall, ev_ms
+    return t
 
 
 def backward_case(torch, fa, w, steps, warmup, seed=0):
@@ -183,14 +190,16 @@ def backward_case(torch, fa, w, steps, warmup, seed=0):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     launch = fa.prepared("fa_bwd", q, k, v, o, lse, do, dq, dk, dv, w.B, w.Hq, w.Hkv, w.Tq,
                          w.Tk, w.d, w.causal_mode, w.scale, stream=stream)
-    wall, ev_ms = time_calls(torch, launch, steps, warmup)
+    t = time_calls(torch, launch, steps, warmup)
     del q, k, v, do, o, lse, dq, dk, dv
-    return wall, ev_ms
+    return t
 
 
-def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
+def decode_case(torch, fa, w, steps, warmup, splits_list, copies=4, seed=0):
     """Decode timed over `copies` independent caches used in rotation, so the
-    last-level cache cannot serve one call's reads from the previous call."""
+    last-level cache cannot serve one call's reads from the previous call.
+    Each requested split count in `splits_list` is timed on the same caches.
+    Returns ({num_splits: timing}, algorithmic bytes per call, cached tokens)."""
     import numpy as np
     from exact_tiled_attention_02_amd import inputs
     seqlens = inputs.decode_seqlens(w, seed=seed)
@@ -223,26 +232,31 @@ def decode_case(torch, fa, w, steps, warmup, num_splits, copies=4, seed=0):
         del caches
         caches = coded
         entry = "fa_decode_fp8" if w.kv_dtype == "fp8" else "fa_decode_int8"
-        calls = [fa.prepared(entry, q, k8, v8, ks, vs, sl, o, w.B, w.Hq, w.Hkv,
-                             w.Tk_max, w.d, num_splits, stream=stream)
-                 for k8, v8, ks, vs in caches]
+
+        def make(ns):
+            return [fa.prepared(entry, q, k8, v8, ks, vs, sl, o, w.B, w.Hq, w.Hkv,
+                                w.Tk_max, w.d, ns, stream=stream) for k8, v8, ks, vs in caches]
         row_bytes = w.d + 4   # codes plus the fp32 row scale, per tensor
     else:
-        calls = [fa.prepared("fa_decode", q, kc, vc, sl, o, w.B, w.Hq, w.Hkv, w.Tk_max, w.d,
-                             num_splits, stream=stream) for kc, vc in caches]
+        def make(ns):
+            return [fa.prepared("fa_decode", q, kc, vc, sl, o, w.B, w.Hq, w.Hkv, w.Tk_max, w.d,
+                                ns, stream=stream) for kc, vc in caches]
         row_bytes = w.d * 2
-    it = [0]
+    out = {}
+    for ns in splits_list:
+        calls = make(ns)
+        it = [0]
 
-    def launch():
-        calls[it[0] % copies]()
-        it[0] += 1
+        def launch():
+            calls[it[0] % copies]()
+            it[0] += 1
 
-    wall, ev_ms = time_calls(torch, launch, steps, warmup)
+        out[ns] = time_calls(torch, launch, steps, warmup)
     kv_bytes = int(seqlens.astype(np.int64).sum()) * w.Hkv * row_bytes * 2
     io_bytes = 2 * w.B * w.Hq * w.d * 2 + w.B * 4
     del caches, q, o
     torch.cuda.empty_cache()
-    return wall, ev_ms, kv_bytes + io_bytes, int(seqlens.sum())
+    return out, kv_bytes + io_bytes, int(seqlens.sum())
 
 
 def read_ceiling(torch, fa, nbytes=1 << 30, copies=2, steps=50, warmup=10):
@@ -258,46 +272,60 @@ def read_ceiling(torch, fa, nbytes=1 << 30, copies=2, steps=50, warmup=10):
         calls[it[0] % copies]()
         it[0] += 1
 
-    _, ev_ms = time_calls(torch, launch, steps, warmup)
+    t = time_calls(torch, launch, steps, warmup)
     del bufs
     torch.cuda.empty_cache()
-    return nbytes / (ev_ms * 1e-3) / 1e9
+    return nbytes / (t["mean_ms"] * 1e-3) / 1e9
 
 
-def cpu_baseline(w, budget_s=12.0, max_s=30.0):
-    """Time the fp64 oracle on whole (batch, head) pairs of the workload until
-    about `budget_s` seconds of CPU work, and scale to TFLOP/s."""
+def cpu_baseline(w, heads=None, max_s=60.0):
+    """Time the fp64 oracle on whole (batch, head) pairs of the workload, one
+    pair per host thread at a time (one-threaded BLAS in each), and scale to
+    TFLOP/s.  By default twice as many pairs as threads; pairs not yet
+    started after about `max_s` seconds of wall-clock are skipped."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     from exact_tiled_attention_02_amd import inputs
-    q, k, v = inputs.prefill_inputs(w)
-    threads = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = sum(i.get("num_threads", 0) for i in threadpool_info()
-                      if i.get("user_api") == "blas") or None
-    except Exception:
-        pass
+        ncpu = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    heads = 2 * threads if heads is None else heads
+    q, k, v = inputs.prefill_inputs(w)
     g = w.Hq // w.Hkv
     per_head = 4.0 * w.Tq * w.Tk * w.d / (2 if w.causal else 1)
-    done = 0
+    order = [(b, h) for b in range(w.B) for h in range(w.Hq)][:heads]
     t0 = time.perf_counter()
-    order = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    for b, h in order:
+
+    def one(bh):
+        b, h = bh
+        if time.perf_counter() - t0 > max_s:
+            return 0
         oracle.softmax_attention(q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1],
                                  v[b:b + 1, h // g:h // g + 1], causal=w.causal, scale=w.scale)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or el >= max_s:
-            break
+        return 1
+
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(1)
+    except Exception:
+        limit = None
+    try:
+        with ThreadPoolExecutor(threads) as ex:
+            done = sum(ex.map(one, order))
+    finally:
+        if limit is not None:
+            limit.restore_original_limits()
     el = time.perf_counter() - t0
     return {
         "value": round(done * per_head / el / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": threads or os.cpu_count(),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} of {len(order)} (batch, head) pairs of {w.name}, all {w.Tq} rows each, "
-                  f"fp64 numpy three-pass, {el:.1f} s",
+        "sample": f"{done} of {w.B * w.Hq} (batch, head) pairs of {w.name}, all {w.Tq} rows each, "
+                  f"fp64 numpy three-pass, one pair per thread on {threads} threads, {el:.1f} s",
     }
 
 
@@ -306,6 +334,37 @@ def inputs_names():
     names = list(inputs.WORKLOADS.keys())
     return names + ["bwd_" + n for n, w in inputs.WORKLOADS.items()
                     if isinstance(w, inputs.Prefill) and w.dtype == "bf16"]
+
+
+def timing_fields(t):
+    return {"kernel_ms": round(t["mean_ms"], 4), "kernel_ms_median": round(t["median_ms"], 4),
+            "kernel_ms_min": round(t["min_ms"], 4)}
+
+
+def prefill_entry(torch, fa, w, name, steps, warmup, kernel):
+    """Time one prefill workload; its roofline block against its dtype's peak."""
+    t = prefill_case(torch, fa, w, steps, warmup)
+    peak = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
+    ach = w.flops / (t["mean_ms"] * 1e-3) / 1e12
+    return t, {"value": round(w.flops / t["wall_s"] / 1e12, 2), "unit": "TFLOP/s",
+               "ms_per_call": round(t["wall_s"] * 1e3, 4), **timing_fields(t),
+               "steps": steps, "dtype": w.dtype,
+               "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                            "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                            "frac_at_min": round(w.flops / (t["min_ms"] * 1e-3) / 1e12 / peak, 4),
+                            "traffic": measured_traffic(name), "kernel": kernel}}
+
+
+# Dominant kernel of each prefill workload (the grid choice of the launcher).
+PREFILL_KERNELS = {
+    "llama3_8b_long": "fwd_bf16_kernel<128, causal, 4, no key split>",
+    "qwen3_0p6b_gqa": "fwd_bf16_kernel<128, causal, 2, key split>",
+    "gpt2_small_mha": "fwd_bf16_kernel<64, causal, 1, no key split>",
+    "llama3_8b_chunk": "fwd_bf16_kernel<128, causal, 4, no key split> (bottom-right)",
+    "gpt2_small_mha_fp8": "fwd_fp8_kernel<64, causal, 1, no key split>",
+    "qwen3_0p6b_gqa_fp8": "fwd_fp8_kernel<128, causal, 2, key split>",
+    "llama3_8b_long_fp8": "fwd_fp8_kernel<128, causal, 4, no key split>",
+}
 
 
 def run_only(torch, fa, inputs, args):
@@ -320,31 +379,66 @@ def run_only(torch, fa, inputs, args):
         del a, b
     if args.only.startswith("bwd_"):
         w = inputs.WORKLOADS[args.only[4:]]
-        wall, ev = backward_case(torch, fa, w, args.steps, args.warmup)
-        out = {"workload": "backward, " + w.name, "TFLOP/s": round(w.bwd_flops / wall / 1e12, 2),
-               "call_ms": round(ev, 4),
-               "frac_of_mfma_peak": round(w.bwd_flops / (ev * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        t = backward_case(torch, fa, w, args.steps, args.warmup)
+        out = {"workload": "backward, " + w.name,
+               "TFLOP/s": round(w.bwd_flops / t["wall_s"] / 1e12, 2), **timing_fields(t),
+               "frac_of_mfma_peak": round(w.bwd_flops / (t["mean_ms"] * 1e-3) / 1e12 /
+                                          PEAK_BF16_TFLOPS, 4)}
         print(json.dumps(out), flush=True)
         return
     w = inputs.WORKLOADS[args.only]
     if isinstance(w, inputs.Prefill):
-        wall, ev = prefill_case(torch, fa, w, args.steps, args.warmup)
-        out = {"workload": w.name, "TFLOP/s": round(w.flops / wall / 1e12, 2),
-               "kernel_ms": round(ev, 4),
-               "frac_of_mfma_peak": round(w.flops / (ev * 1e-3) / 1e12 /
-                                          (PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS), 4)}
+        t = prefill_case(torch, fa, w, args.steps, args.warmup)
+        peak = PEAK_FP8_TFLOPS if w.dtype == "fp8" else PEAK_BF16_TFLOPS
+        out = {"workload": w.name, "TFLOP/s": round(w.flops / t["wall_s"] / 1e12, 2),
+               **timing_fields(t),
+               "frac_of_mfma_peak": round(w.flops / (t["mean_ms"] * 1e-3) / 1e12 / peak, 4)}
     else:
-        wall, ev, nbytes, _ = decode_case(torch, fa, w, args.steps, args.warmup, args.decode_splits)
-        out = {"workload": w.name, "GB/s": round(nbytes / (ev * 1e-3) / 1e9, 1),
-               "call_us": round(ev * 1e3, 2), "num_splits": args.decode_splits}
+        res, nbytes, _ = decode_case(torch, fa, w, args.steps, args.warmup, [args.decode_splits])
+        t = res[args.decode_splits]
+        out = {"workload": w.name, "GB/s": round(nbytes / (t["mean_ms"] * 1e-3) / 1e9, 1),
+               "call_us": round(t["mean_ms"] * 1e3, 2), "num_splits": args.decode_splits}
     print(json.dumps(out), flush=True)
+
+
+def decode_entry(fa, w, res, nbytes, ntok, auto, ceil_gbs, plan, key):
+    """JSON block of one decode workload: the automatic split count's
+    roofline and, for the bf16 cache, every timed split count."""
+    t = res[0]
+    gbs = nbytes / (t["mean_ms"] * 1e-3) / 1e9
+    blk = {"value": round(nbytes / t["wall_s"] / 1e9, 1), "unit": "GB/s",
+           "read_probe_gbs": round(ceil_gbs, 1), "frac_of_read_probe": round(gbs / ceil_gbs, 4),
+           "us_per_call": round(t["wall_s"] * 1e6, 2), "call_us_events": round(t["mean_ms"] * 1e3, 2),
+           "call_us_median": round(t["median_ms"] * 1e3, 2),
+           "call_us_min": round(t["min_ms"] * 1e3, 2),
+           "num_splits": auto, "algorithmic_bytes": nbytes, "kv_tokens": ntok,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": measured_traffic(key)}}
+    if len(res) > 1:
+        sweep = {}
+        for ns, ts in res.items():
+            if ns == 0:
+                continue
+            g = nbytes / (ts["mean_ms"] * 1e-3) / 1e9
+            sweep[str(ns)] = {"key_ranges": plan(w.B, w.Hq, w.Hkv, w.Tk_max, w.d, ns),
+                              "call_us_events": round(ts["mean_ms"] * 1e3, 2),
+                              "call_us_median": round(ts["median_ms"] * 1e3, 2),
+                              "call_us_min": round(ts["min_ms"] * 1e3, 2),
+                              "GB/s": round(g, 1), "frac_of_hbm_peak": round(g / PEAK_HBM_GBS, 4)}
+        blk["num_splits_sweep"] = {
+            "note": "num_splits is the number of equal key ranges the whole batch's key space "
+                    f"(all {w.B} sequences x {w.Hkv} kv heads) is cut into, one workgroup each; "
+                    f"the automatic choice ({auto}) is the device's resident workgroup count",
+            **sweep}
+    return blk
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="num_splits for decode (0 = library choice)")
@@ -371,20 +465,20 @@ def main():
         run_only(torch, fa, inputs, args)
         return
 
-    w = inputs.GPT2_SMALL_MHA
+    w = inputs.LLAMA3_8B_LONG
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
-    wall, ev_ms = prefill_case(torch, fa, w, args.steps, args.warmup)
-    value = w.flops / wall / 1e12
-    achieved = w.flops / (ev_ms * 1e-3) / 1e12
-    traffic = measured_traffic("gpt2_small_mha")
+    t, blk = prefill_entry(torch, fa, w, "llama3_8b_long", args.steps, args.warmup,
+                           PREFILL_KERNELS["llama3_8b_long"])
+    roof = dict(blk["roofline"])
+    roof.update(timing_fields(t))
     result = {
         "metric": "causal prefill attn TFLOP/s (% MFMA peak); decode HBM GB/s (% peak)",
-        "value": round(value, 2),
+        "value": blk["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3, 4),
+        "ms_per_step": round(t["wall_s"] * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -392,74 +486,54 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Tq": w.Tq,
                    "Tk": w.Tk, "d": w.d, "causal": w.causal, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "fwd_bf16_kernel<64, causal, 1, no key split>",
-                     "kernel_ms": round(ev_ms, 4)},
+        "roofline": roof,
     }
-    log(f"[bench] headline {value:.1f} TFLOP/s, kernel {ev_ms:.3f} ms")
+    log(f"[bench] headline {blk['value']:.1f} TFLOP/s, kernel {t['mean_ms']:.3f} ms "
+        f"(median {t['median_ms']:.3f}, min {t['min_ms']:.3f})")
 
     if not args.no_extra:
         also = {}
-        for name, steps in (("qwen3_0p6b_gqa", max(10, args.steps)), ("llama3_8b_long", 10),
-                            ("llama3_8b_chunk", 20), ("gpt2_small_mha_fp8", max(10, args.steps)),
-                            ("qwen3_0p6b_gqa_fp8", max(10, args.steps)),
-                            ("llama3_8b_long_fp8", 10)):
+        for name, steps in (("qwen3_0p6b_gqa", 200), ("gpt2_small_mha", 100),
+                            ("llama3_8b_chunk", 30), ("gpt2_small_mha_fp8", 100),
+                            ("qwen3_0p6b_gqa_fp8", 200), ("llama3_8b_long_fp8", 10)):
             wk = inputs.WORKLOADS[name]
             log(f"[bench] {wk.name}")
-            wl, ev = prefill_case(torch, fa, wk, steps, max(2, min(args.warmup, steps)))
-            ach = wk.flops / (ev * 1e-3) / 1e12
-            peak = PEAK_FP8_TFLOPS if wk.dtype == "fp8" else PEAK_BF16_TFLOPS
-            also[name] = {"value": round(wk.flops / wl / 1e12, 2), "unit": "TFLOP/s",
-                          "ms_per_call": round(wl * 1e3, 4), "kernel_ms": round(ev, 4),
-                          "frac_of_mfma_peak": round(ach / peak, 4),
-                          "mfma_peak": peak, "dtype": wk.dtype,
-                          "traffic": measured_traffic(name)}
+            _, also[name] = prefill_entry(torch, fa, wk, name, steps, 10, PREFILL_KERNELS[name])
             log(f"[bench]   {also[name]}")
         for name, steps in (("gpt2_small_mha", 20), ("qwen3_0p6b_gqa", 20), ("llama3_8b_long", 3)):
             wk = inputs.WORKLOADS[name]
             log(f"[bench] backward, {wk.name}")
-            wl, ev = backward_case(torch, fa, wk, steps, 2)
-            ach = wk.bwd_flops / (ev * 1e-3) / 1e12
-            also["bwd_" + name] = {"value": round(wk.bwd_flops / wl / 1e12, 2), "unit": "TFLOP/s",
+            tb = backward_case(torch, fa, wk, steps, 2)
+            ach = wk.bwd_flops / (tb["mean_ms"] * 1e-3) / 1e12
+            also["bwd_" + name] = {"value": round(wk.bwd_flops / tb["wall_s"] / 1e12, 2),
+                                   "unit": "TFLOP/s",
                                    "flops": "10*B*Hq*Tq*Tk*d/2 (five products, causal)",
-                                   "ms_per_call": round(wl * 1e3, 4), "call_ms_events": round(ev, 4),
+                                   "ms_per_call": round(tb["wall_s"] * 1e3, 4),
+                                   "call_ms_events": round(tb["mean_ms"], 4),
+                                   "call_ms_median": round(tb["median_ms"], 4),
+                                   "call_ms_min": round(tb["min_ms"], 4),
                                    "frac_of_mfma_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
             log(f"[bench]   {also['bwd_' + name]}")
-        wd = inputs.FLASH_DECODE
-        S = fa.fa_decode_workgroups(wd.B, wd.Hq, wd.Hkv, wd.Tk_max, wd.d, args.decode_splits)
-        log(f"[bench] {wd.name}, {S} key ranges")
-        wl, ev, nbytes, ntok = decode_case(torch, fa, wd, 200, 100, args.decode_splits)
-        gbs = nbytes / (ev * 1e-3) / 1e9
         ceil_gbs = read_ceiling(torch, fa)
         log(f"[bench] read probe (1 GiB streamed once): {ceil_gbs:.1f} GB/s")
-        also["flash_decode"] = {"value": round(nbytes / wl / 1e9, 1), "unit": "GB/s",
-                                "read_probe_gbs": round(ceil_gbs, 1),
-                                "frac_of_read_probe": round(gbs / ceil_gbs, 4),
-                                "us_per_call": round(wl * 1e6, 2), "call_us_events": round(ev * 1e3, 2),
-                                "num_splits": S, "algorithmic_bytes": nbytes, "kv_tokens": ntok,
-                                "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
-                                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                             "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                             "traffic": measured_traffic("flash_decode")}}
+        wd = inputs.FLASH_DECODE
+        auto = fa.fa_decode_workgroups(wd.B, wd.Hq, wd.Hkv, wd.Tk_max, wd.d, args.decode_splits)
+        log(f"[bench] {wd.name}, {auto} key ranges, and a sweep of num_splits")
+        splits = [args.decode_splits] + [n for n in (8, 16, 32, 64, 128, 256, 1024)
+                                         if n != args.decode_splits]
+        res, nbytes, ntok = decode_case(torch, fa, wd, 100, 20, splits)
+        res = {(0 if ns == args.decode_splits else ns): r for ns, r in res.items()}
+        also["flash_decode"] = decode_entry(fa, wd, res, nbytes, ntok, auto, ceil_gbs,
+                                            fa.fa_decode_workgroups, "flash_decode")
         log(f"[bench]   {also['flash_decode']}")
         for key, w8, plan in (("flash_decode_fp8", inputs.FLASH_DECODE_FP8, fa.fa_decode_fp8_workgroups),
                               ("flash_decode_int8", inputs.FLASH_DECODE_INT8, fa.fa_decode_int8_workgroups)):
-            S8 = plan(w8.B, w8.Hq, w8.Hkv, w8.Tk_max, w8.d, args.decode_splits)
-            log(f"[bench] {w8.name}, {S8} key ranges")
-            wl8, ev8, nbytes8, ntok8 = decode_case(torch, fa, w8, 200, 100, args.decode_splits)
-            gbs8 = nbytes8 / (ev8 * 1e-3) / 1e9
-            also[key] = {"value": round(nbytes8 / wl8 / 1e9, 1), "unit": "GB/s",
-                         "read_probe_gbs": round(ceil_gbs, 1),
-                         "frac_of_read_probe": round(gbs8 / ceil_gbs, 4),
-                         "us_per_call": round(wl8 * 1e6, 2),
-                         "call_us_events": round(ev8 * 1e3, 2), "num_splits": S8,
-                         "algorithmic_bytes": nbytes8, "kv_tokens": ntok8,
-                         "speedup_vs_bf16_cache": round(ev / ev8, 3),
-                         "roofline": {"bound": "hbm", "achieved": round(gbs8, 1),
-                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                      "frac": round(gbs8 / PEAK_HBM_GBS, 4),
-                                      "traffic": measured_traffic(key)}}
+            a8 = plan(w8.B, w8.Hq, w8.Hkv, w8.Tk_max, w8.d, args.decode_splits)
+            log(f"[bench] {w8.name}, {a8} key ranges")
+            r8, nb8, nt8 = decode_case(torch, fa, w8, 200, 50, [args.decode_splits])
+            r8 = {0: r8[args.decode_splits]}
+            also[key] = decode_entry(fa, w8, r8, nb8, nt8, a8, ceil_gbs, plan, key)
+            also[key]["speedup_vs_bf16_cache"] = round(res[0]["mean_ms"] / r8[0]["mean_ms"], 3)
             log(f"[bench]   {also[key]}")
         result["also"] = also
 
