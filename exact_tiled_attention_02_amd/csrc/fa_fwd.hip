@@ -421,13 +421,13 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
         nmc = nmc_new;
         thr = m + lazy_raw;
       }
-      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      float ls[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           s[kb][r] = exp2_fast(fmaf(s[kb][r], c, nmc));
-          ls[r & 3] += s[kb][r];
+          ls[r & 3] = kb == 0 && r < 4 ? s[kb][r] : ls[r & 3] + s[kb][r];   // four partial sums
         }
       l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
