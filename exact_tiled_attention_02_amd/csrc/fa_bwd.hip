@@ -25,14 +25,14 @@
 //     L_i * log2(e), into a workspace whose per-head planes are padded with
 //     zero rows to a multiple of kBwdRowPad.
 //  2. bwd_dkdv: a workgroup owns 128 keys of one kv head, 32 per wavefront.
-//     K and V stay in registers and dK^T, dV^T in accumulators while tiles of
-//     64 query rows (Q, dO, L, D) of every query head of the group stream
-//     through LDS, the next tile copied while the current one is used.  Per
-//     32 query rows a wavefront forms S = Q K^T and dP = dO V^T (lane = key,
-//     registers = queries), P and dS in registers, then dV^T += dO^T P and
-//     dK^T += Q^T dS with dO^T and Q^T read through the transposing LDS read.
-//     Under the causal mask the query rows that see none of the workgroup's
-//     keys are never visited and 32x32 blocks above the diagonal are skipped.
+//     K and V stay in registers and dK^T, dV^T in AGPR accumulators while
+//     blocks of 32 query rows (Q, dO, L, D) of every query head of the group
+//     stream through an LDS ring.  Per block a wavefront forms S = Q K^T and
+//     dP = dO V^T (lane = key, registers = queries), P and dS on the VALU,
+//     then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read through
+//     the transposing LDS read; the three steps of consecutive blocks are
+//     software-pipelined (see the kernel).  Under the causal mask the query
+//     rows that see none of the workgroup's keys are never visited.
 //  3. bwd_dq: a workgroup owns 32*NW query rows of one query head; Q and dO
 //     stay in registers and dQ^T in accumulators while tiles of 64 keys (K,
 //     V) stream through LDS.  Per 32 keys: S^T = K Q^T and dP^T = V dO^T
@@ -211,20 +211,132 @@ __global__ void __launch_bounds__(kPrepThreads) bwd_prep_kernel(const BwdParams 
 // ---------------------------------------------------------------------------
 // 2. dK and dV
 // ---------------------------------------------------------------------------
+// A workgroup owns 128 keys of one kv head, 32 per wavefront, with K and V
+// rows in registers and dK^T, dV^T in AGPR accumulators (lane = key).  Its
+// work is a sequence of 32-row query blocks -- every query head of the
+// group, the rows that can see its keys -- and each block passes three
+// steps, software-pipelined so that iteration k of the loop runs
+//   phase 1: X(k)   S = Q K^T and dP = dO V^T of block k, with dS = P (dP - D)
+//            of block k-1 and the bf16 packing of its P and dS on the VALU;
+//   phase 2: Z(k-1) dV^T += dO^T P and dK^T += Q^T dS of block k-1, with
+//            P = 2^(S c - L) of block k on the VALU,
+// one or two VALU elements per matrix-core product, so that exponentials and
+// conversions issue between independent products.  S and dP stay in AGPRs
+// until the VALU reads them (dP alternates between two sets: dS of block k-1
+// reads one while X(k) fills the other).  Rows of Q and dO, and the L and D
+// values, stream through LDS rings of 5 stages; Z reads block k-1's rows with
+// the transposing read.  Between the phases every wavefront waits for its
+// copies of block k+1, the workgroup meets, and the copies of block k+3 are
+// issued into the stage block k-2 used.  Iterations before the first block
+// and after the last (pipeline fill and drain, and padding to an even count)
+// compute with P = 0 on the data of a real block, so they add exactly zero.
+
+// Copy 16 bytes per lane from a buffer resource (lane offset voff, range
+// checked) or from global memory straight into LDS at lds + 16 * lane (lds
+// the same for the whole wavefront).
+__device__ __forceinline__ void buf_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(size_t)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void glb_to_lds(const void* src, uint32_t lds) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(size_t)lds, 16, 0, 0);
+}
+
+// acc += a * b on the bf16 matrix core, accumulator in AGPRs.
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// acc = a * b on the bf16 matrix core, into AGPRs.
+__device__ __forceinline__ void mfma_new(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+
+// One accumulator register read into a VGPR where it stands in the program.
+__device__ __forceinline__ float acc_read(const float& a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+__device__ __forceinline__ void agpr_zero(f32x16& acc) {
+  asm volatile("" : "=a"(acc) : "0"(f32x16{}));
+}
+
+// LDS read schedule of a dK/dV iteration.  Slot m (0 .. 2NS-1; the product
+// of slot m is the X product m for m < NS, else the Z product m - NS) first
+// issues the reads of operand m + LA -- X operands are one 16-byte read,
+// Z operands two transposing reads, operands past the iteration's end are
+// the next iteration's first ones -- then at slot NS/2 the 4 reads of the
+// block's L and at slot NS + NS/2 the 4 reads of its D.  wait[m] is the
+// lgkmcnt the product of slot m waits for: every read of its operand done,
+// and at slot NS also L, at slot 0 also the previous iteration's D.
+template <int NS, int LA>
+struct DkdvSchedule {
+  int wait[2 * NS];
+  constexpr DkdvSchedule() : wait() {
+    const int slr = NS / 2, sdr = NS + NS / 2;
+    int last[4][2 * NS] = {};   // issue index of the last read of (iteration, operand)
+    int issued[3][2 * NS] = {}; // reads issued through slot m's issues
+    int lread[3] = {}, dread[3] = {};
+    int n = 0;
+    for (int it = 0; it < 3; ++it) {
+      for (int m = 0; m < 2 * NS; ++m) {
+        int f = m + LA, ti = it;
+        if (f >= 2 * NS) {
+          f -= 2 * NS;
+          ti = it + 1;
+        }
+        n += f < NS ? 1 : 2;
+        last[ti][f] = n - 1;
+        if (m == slr) {
+          n += 4;
+          lread[it] = n - 1;
+        }
+        if (m == sdr) {
+          n += 4;
+          dread[it] = n - 1;
+        }
+        issued[it][m] = n;
+      }
+    }
+    for (int m = 0; m < 2 * NS; ++m) {
+      int w = issued[2][m] - 1 - last[2][m];
+      if (m == NS && issued[2][m] - 1 - lread[2] < w) w = issued[2][m] - 1 - lread[2];
+      if (m == 0 && issued[2][m] - 1 - dread[1] < w) w = issued[2][m] - 1 - dread[1];
+      wait[m] = w;
+    }
+  }
+};
+
+template <int NS, int LA>
+constexpr bool dkdv_schedule_ok() {
+  constexpr DkdvSchedule<NS, LA> s{};
+  for (int m = 0; m < 2 * NS; ++m)
+    if (s.wait[m] < 0 || s.wait[m] > 15) return false;
+  return true;
+}
+
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NW = kDkdvThreads / 64;
-  constexpr int NC = D / 16;                         // 16-deep steps over the head dim
-  constexpr int ND = D / 32;                         // 32-wide output blocks
-  constexpr int CPR = D / 8;                         // 16-byte chunks per row
-  constexpr int TB = kQTile * D * 2;                 // bytes of a Q or dO tile
-  constexpr int NCOPY = kQTile * CPR / kDkdvThreads; // copies per thread, tile and tensor
-  constexpr int LDB = 2 * kQTile * 4;                // bytes of a tile's L and D rows
-  constexpr int QOFF = 2 * LDB;                      // LDS: [L,D x2 | Q,dO stage 0 | Q,dO stage 1]
-  constexpr int SB = 2 * TB;
-  static_assert(NCOPY >= 1, "tile too small for the workgroup");
-  static_assert(QOFF + SB + TB + 48 * D * 2 < 65536, "operand offsets must fit the immediate");
-  __shared__ __attribute__((aligned(16))) char lds[QOFF + 2 * SB];
+  constexpr int NC = D / 16;                     // 16-deep steps over the head dim
+  constexpr int ND = D / 32;                     // 32-wide head-dim blocks
+  constexpr int NS = D / 8;                      // products per phase (2 NC = 4 ND)
+  constexpr int EPS = 16 / NS;                   // P or dS elements per product
+  constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  constexpr int RB = 32 * D * 2;                 // bytes of 32 rows of Q or dO
+  constexpr int SBY = 2 * RB;                    // a stage: [Q | dO]
+  constexpr int NST = 5;                         // stages per ring
+  constexpr int LDR = NST * SBY;                 // L/D ring: stage = [L x32 | D x32] fp32
+  constexpr int NCR = 32 * CPR / kDkdvThreads;   // row copies per thread and tensor
+  constexpr int NV = 2 * NCR + 1;                // vector-memory instructions per iteration
+  constexpr int LA = 4;                          // operands read ahead of their product
+  constexpr int SLR = NS / 2;                    // slot that reads L of block k
+  constexpr int SDR = NS + NS / 2;               // slot that reads D of block k
+  static_assert(NCR >= 1, "tile too small for the workgroup");
+  static_assert(dkdv_schedule_ok<NS, LA>(), "LDS read schedule exceeds the wait counter");
+  constexpr DkdvSchedule<NS, LA> sched{};
+  __shared__ __attribute__((aligned(16))) char lds[LDR + NST * 256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -252,196 +364,279 @@ __global__ void __launch_bounds__(kDkdvThreads, 1) bwd_dkdv_kernel(const BwdPara
 
   f32x16 dv[ND], dk[ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dv[i][r] = 0.f;
-      dk[i][r] = 0.f;
-    }
+  for (int i = 0; i < ND; ++i) {
+    agpr_zero(dv[i]);
+    agpr_zero(dk[i]);
+  }
 
-  // Query tiles: rows qs .. Tq-1 of each of the g query heads.  Causal: row i
-  // sees key j iff j <= i + off, so rows before k0 - off see none of these
-  // keys (qs is kept a multiple of the tile height).
+  // Blocks: rows qs + 32*i .. +31 of each of the g query heads, item
+  // it = head * nblk + i.  Causal: row i sees key j iff j <= i + off, so rows
+  // before k0 - off see none of these keys.
   const int off = p.causal_off;
-  const int qs = CAUSAL ? max(0, k0 - off) / kQTile * kQTile : 0;
-  const int ntq = qs < p.Tq ? (p.Tq - qs + kQTile - 1) / kQTile : 0;
-  const int nit = p.g * ntq;
-  // This workgroup's items (query head it / ntq, query tile it % ntq).
+  const int qs = CAUSAL ? max(0, k0 - off) / 32 * 32 : 0;
+  const int nblk = qs < p.Tq ? (p.Tq - qs + 31) / 32 : 0;
+  const int nit = p.g * nblk;
   const int i0 = (int)((long long)nit * part / p.kparts);
   const int i1 = (int)((long long)nit * (part + 1) / p.kparts);
 
-  // Copy r of wavefront w fills LDS chunks [(r*NW + w)*64, +64) of a tile:
-  // chunk L is row L / CPR at position L % CPR, holding chunk
-  // (L % CPR) ^ bswz(row) of that row.
-  uint32_t csrc[NCOPY];
+  if (i1 > i0) {
+    // Copy r of wavefront w fills LDS chunks [(r*NW + w)*64, +64) of a row
+    // tile: chunk L is row L / CPR at position L % CPR, holding chunk
+    // (L % CPR) ^ bswz(row) of that row.
+    uint32_t csrc[NCR];
 #pragma unroll
-  for (int r = 0; r < NCOPY; ++r) {
-    const int L = (r * NW + wave) * 64 + lane;
-    const int row = L / CPR;
-    csrc[r] = (uint32_t)(row * D + (((L % CPR) ^ bswz<D>(row)) << 3)) * 2u;
-  }
-  const int qbytes = p.Tq * D * 2;
-  auto issue = [&](int it, auto st_c) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    const int hq = kvh * p.g + it / ntq;
-    const int q0 = qs + (it % ntq) * kQTile;
-    const size_t plane = (size_t)b * p.Hq + hq;
-    // Rows past Tq read as zeros (the whole offset is in the range-checked
-    // lane offset).
-    const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const bf16*)p.q + plane * p.Tq * D), 0, qbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const bf16*)p.dout + plane * p.Tq * D), 0, qbytes, 0x00020000);
-    const uint32_t base = (uint32_t)q0 * D * 2;
-    char* qd = lds + QOFF + ST * SB;
-#pragma unroll
-    for (int r = 0; r < NCOPY; ++r) {
-      copy16_buf_to_lds(qr, qd + (r * NW + wave) * 1024, csrc[r] + base, 0);
-      copy16_buf_to_lds(gr, qd + TB + (r * NW + wave) * 1024, csrc[r] + base, 0);
+    for (int r = 0; r < NCR; ++r) {
+      const int L = (r * NW + wave) * 64 + lane;
+      const int row = L / CPR;
+      csrc[r] = (uint32_t)(row * D + (((L % CPR) ^ bswz<D>(row)) << 3)) * 2u;
     }
-    // L and D of the 64 rows (padded planes: always in bounds): wavefronts
-    // 0,1 copy L, 2,3 copy D, 32 values each with 8 lanes.
-    const float* src = (wave < 2 ? p.l2 : p.delta) + plane * p.Tqp + q0 + 32 * (wave & 1) + 4 * lane;
-    if (lane < 8) copy16_to_lds(src, lds + ST * LDB + (wave >> 1) * 256 + (wave & 1) * 128);
-  };
-
-  const TileReads<D> rd(lds_addr(lds), lane);
-  const uint32_t lrd = lds_addr(lds) + 16 * half;   // L/D rows 8j + 4*half .. +3
-  const float c = p.c;
-
-  // 32 query rows (half HF of the stage-ST tile whose first row is q0).
-  // MK: 0 no mask, 1 mask, 2 decided at run time by mask_rt (one code path;
-  // at d = 128 separate paths cost registers and were slower).
-  auto rows32 = [&](int q0h, auto st_c, auto hf_c, auto mk_c, bool mask_rt) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    constexpr int HF = decltype(hf_c)::value;
-    constexpr int MK = decltype(mk_c)::value;
-    constexpr int QT = QOFF + ST * SB + HF * 32 * D * 2;   // Q rows of this half
-    constexpr int GT = QT + TB;                            // dO rows
-    constexpr int LT = ST * LDB + HF * 32 * 4;             // L rows; D at +256
-
-    // S = Q K^T and dP = dO V^T: lane = key, register r = query row
-    // 8*(r/4) + 4*half + r%4 of this half.
-    bf16x8 a[NC];
-    f32x4 lv[4], dl[4];
-    static_for<0, NC>([&](auto s_c) { a[s_c] = lds_read_b128<QT>(rd.row[s_c]); });
-    static_for<0, 4>([&](auto j_c) { lv[j_c] = lds_read_f32x4<LT + 32 * j_c>(lrd); });
-    lgkm_wait<0>();
-#pragma unroll
-    for (int s = 0; s < NC; ++s) tie(a[s]);
-    bf16x8 g[NC];
-    static_for<0, NC>([&](auto s_c) { g[s_c] = lds_read_b128<GT>(rd.row[s_c]); });
-    static_for<0, 4>([&](auto j_c) { dl[j_c] = lds_read_f32x4<LT + 256 + 32 * j_c>(lrd); });
-    f32x16 sc = {};
-#pragma unroll
-    for (int s = 0; s < NC; ++s) sc = mma_32x32x16(a[s], kf[s], sc);
-    lgkm_wait<0>();
-#pragma unroll
-    for (int s = 0; s < NC; ++s) tie(g[s]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      tie(lv[j]);
-      tie(dl[j]);
-    }
-    f32x16 dp = {};
-#pragma unroll
-    for (int s = 0; s < NC; ++s) dp = mma_32x32x16(g[s], vf[s], dp);
-
-    // P = exp(S*scale - L) (base 2), dS = P (dP - D).
-    float pv[16], ds[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = exp2_fast(fmaf(sc[r], c, -lv[r >> 2][r & 3]));
-    if (MK == 1 || (MK == 2 && mask_rt)) {
-      // Row offsets 8*(r/4) + r%4 outside [lo, hi) are masked: rows past
-      // Tq, and under the causal mask rows before this lane's key.
-      const int base = q0h + 4 * half;
-      const int lo = CAUSAL ? my_k - off - base : -64;
-      const int hi = p.Tq - base;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 8 * (r >> 2) + (r & 3);
-        pv[r] = (off >= lo && off < hi) ? pv[r] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ds[r] = pv[r] * (dp[r] - dl[r >> 2][r & 3]);
-    const bf16x8 pb[2] = {pack8(pv), pack8(pv + 8)};
-    const bf16x8 sb[2] = {pack8(ds), pack8(ds + 8)};
-
-    // dV^T += dO^T P and dK^T += Q^T dS over the 32 rows, in four groups
-    // (tensor, 16-row step j); the reads of the next group are in flight
-    // while the current one multiplies.
-    auto tr_issue = [&](auto t_c, auto j_c, u32x2 (&v)[ND][2]) __attribute__((always_inline)) {
-      constexpr int OFF = (decltype(t_c)::value == 0 ? GT : QT) + decltype(j_c)::value * 16 * D * 2;
-      static_for<0, ND>([&](auto db_c) {
-        v[db_c][0] = lds_read_tr<OFF>(rd.tr[0][db_c]);
-        v[db_c][1] = lds_read_tr<OFF>(rd.tr[1][db_c]);
-      });
+    const int qbytes = p.Tq * D * 2;
+    // Base of this wavefront's 1 KB of every tile in LDS, passed through an
+    // empty statement once per iteration so that the compiler forms each
+    // copy's destination there instead of holding them all in scalar
+    // registers for the whole loop.
+    uint32_t lb = lds_addr(lds) + wave * 1024;
+    // A plane's base address in scalar registers (the compiler may hold
+    // loop-invariant parts of it in vector registers, and a buffer descriptor
+    // built from those would be treated as divergent).
+    auto plane_ptr = [&](const void* base, size_t elems) __attribute__((always_inline)) {
+      const uint64_t a = (uint64_t)(uintptr_t)((const bf16*)base + elems);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+      return (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
     };
-    auto tr_tie = [&](u32x2 (&v)[ND][2]) __attribute__((always_inline)) {
+    // Rows of Q and dO (rows past Tq read as zeros: the whole offset is in
+    // the range-checked lane offset), and L and D (padded planes: always in
+    // bounds; wavefronts 0, 1 copy L, 2, 3 copy D, 16 values each with 4
+    // lanes) of the block at (plane, q0) into stage st.
+    auto copy_block = [&](int plane, int q0, int st) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+          plane_ptr(p.q, (size_t)plane * p.Tq * D), 0, qbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t gr = __builtin_amdgcn_make_buffer_rsrc(
+          plane_ptr(p.dout, (size_t)plane * p.Tq * D), 0, qbytes, 0x00020000);
+      const uint32_t base = (uint32_t)q0 * D * 2;
+      const uint32_t sb = lb + (uint32_t)(st * SBY);
 #pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        tie(v[db][0]);
-        tie(v[db][1]);
+      for (int r = 0; r < NCR; ++r) {
+        buf_to_lds(qr, sb + r * NW * 1024, csrc[r] + base);
+        buf_to_lds(gr, sb + RB + r * NW * 1024, csrc[r] + base);
+      }
+      const float* src = (wave < 2 ? p.l2 : p.delta) + (size_t)plane * p.Tqp + q0 + 16 * (wave & 1) + 4 * lane;
+      if (lane < 4) glb_to_lds(src, lb - wave * 1024 + LDR + st * 256 + 64 * wave);
+    };
+
+    // Walk over the blocks in sequence: item it = h * nblk + i runs from i0
+    // to i1 - 1, and blocks outside [i0, i1) stand on the nearest end.
+    struct Walk {
+      int h, i;
+    };
+    const int plane0 = b * p.Hq + kvh * p.g;
+    auto walk_start = [&]() __attribute__((always_inline)) {
+      const int h = i0 / nblk;
+      return Walk{h, i0 - h * nblk};
+    };
+    auto walk_to = [&](Walk& w, int j) __attribute__((always_inline)) {   // w is at block j - 1
+      if (j > i0 && j < i1) {
+        if (++w.i == nblk) {
+          w.i = 0;
+          ++w.h;
+        }
       }
     };
-    auto tr_mul = [&](auto t_c, auto j_c, u32x2 (&v)[ND][2]) __attribute__((always_inline)) {
-      constexpr int J = decltype(j_c)::value;
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        if constexpr (decltype(t_c)::value == 0)
-          dv[db] = mma_32x32x16(join_tr(v[db]), pb[J], dv[db]);
-        else
-          dk[db] = mma_32x32x16(join_tr(v[db]), sb[J], dk[db]);
-      }
-    };
-    u32x2 va[ND][2], vb[ND][2];
-    tr_issue(IC<0>{}, IC<0>{}, va);
-    lgkm_wait<0>();
-    tr_tie(va);
-    tr_issue(IC<0>{}, IC<1>{}, vb);
-    tr_mul(IC<0>{}, IC<0>{}, va);
-    lgkm_wait<0>();
-    tr_tie(vb);
-    tr_issue(IC<1>{}, IC<0>{}, va);
-    tr_mul(IC<0>{}, IC<1>{}, vb);
-    lgkm_wait<0>();
-    tr_tie(va);
-    tr_issue(IC<1>{}, IC<1>{}, vb);
-    tr_mul(IC<1>{}, IC<0>{}, va);
-    lgkm_wait<0>();
-    tr_tie(vb);
-    tr_mul(IC<1>{}, IC<1>{}, vb);
-  };
+    auto next_st = [](int s) __attribute__((always_inline)) { return s == NST - 1 ? 0 : s + 1; };
 
-  auto step = [&](int it, auto st_c) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    // Tile `it` has landed (every wavefront waits for its own copies, then
-    // all meet), and nobody reads stage ST^1 any more.
+    // Per-lane LDS read bases at stage 0 (iterations add the stage).
+    const TileReads<D> rd(lds_addr(lds), lane);
+    const uint32_t la0 = lds_addr(lds) + LDR + 16 * half;   // L/D rows 8j + 4*half .. +3
+    const float c = p.c;
+
+    // Iterations k = kbeg .. i1 (an even count).
+    const int niter = (i1 - i0 + 2) / 2 * 2;
+    const int kbeg = i1 + 1 - niter;
+    Walk cw = walk_start();   // copies: block kbeg - 1 first
+    Walk mw = walk_start();   // masks: block kbeg first
+    copy_block(plane0 + cw.h, qs + 32 * cw.i, NST - 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      walk_to(cw, kbeg + j);
+      copy_block(plane0 + cw.h, qs + 32 * cw.i, j);
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-    tile_barrier();
-    if (it + 1 < i1) issue(it + 1, IC<ST ^ 1>{});
-    const int q0 = qs + (it % ntq) * kQTile;
-    static_for<0, 2>([&](auto hf_c) {
-      const int q0h = q0 + 32 * hf_c;
-      // Under the causal mask query i sees key j iff j <= i + off.  Blocks
-      // with every key after every row's limit are skipped; only blocks that
-      // cross the diagonal and the last rows need the mask.
-      if (CAUSAL && q0h + 31 + off < kw) return;
-      const bool mask = (CAUSAL && q0h + off < kw + 31) || q0h + 32 > p.Tq;
-      if constexpr (D == 128)
-        rows32(q0h, st_c, hf_c, IC<2>{}, mask);
-      else if (mask)
-        rows32(q0h, st_c, hf_c, IC<1>{}, true);
-      else
-        rows32(q0h, st_c, hf_c, IC<0>{}, false);
-    });
-  };
-  if (i1 > i0) issue(i0, IC<0>{});
-  for (int it = i0; it < i1; it += 2) {
-    step(it, IC<0>{});
-    if (it + 1 < i1) step(it + 1, IC<1>{});
+    asm volatile("s_barrier" ::: "memory");
+
+    int st = 0;   // stage of block k
+    uint32_t rk[NC];
+#pragma unroll
+    for (int s = 0; s < NC; ++s) rk[s] = rd.row[s];
+    f32x16 sc, dp[2];
+    agpr_zero(dp[1]);
+    float pv[16];
+    f32x4 lv[4], dl[4];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pv[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 pre[LA];
+    // X operands of the first iteration, as the iteration before would have
+    // read them.
+    auto read_x = [&](const uint32_t (&r)[NC], auto f_c) __attribute__((always_inline)) {
+      constexpr int F = decltype(f_c)::value;
+      return lds_read_b128<(F % 2) * RB>(r[F / 2]);
+    };
+    static_for<0, LA>([&](auto f_c) { pre[f_c] = read_x(rk, f_c); });
+
+    auto iteration = [&](const int k, auto par_c) __attribute__((always_inline)) {
+      constexpr int P = decltype(par_c)::value;   // dP set written by X(k)
+      const int stp = st == 0 ? NST - 1 : st - 1;  // stage of block k-1
+      const int stn = next_st(st);                 // stage of block k+1
+      uint32_t zk[2][ND], rn[NC];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) zk[e][db] = rd.tr[e][db] + (uint32_t)(stp * SBY);
+#pragma unroll
+      for (int s = 0; s < NC; ++s) rn[s] = rd.row[s] + (uint32_t)(stn * SBY);
+      const uint32_t la = la0 + (uint32_t)(st * 256);
+      walk_to(mw, k);
+      const int qy = qs + 32 * mw.i;
+      const bool yvalid = k >= i0 && k < i1;
+      const bool ymask = !yvalid || (CAUSAL && qy + off < kw + 31) || qy + 32 > p.Tq;
+
+      bf16x8 cur[2 * NS];
+      float dsv[16];
+      uint32_t pw[8], sw[8];
+      auto read_z = [&](auto f_c) __attribute__((always_inline)) {
+        constexpr int G = decltype(f_c)::value - NS;
+        constexpr int T = G / (2 * ND);   // 0: dO^T (dV), 1: Q^T (dK)
+        constexpr int J = (G / ND) % 2;
+        constexpr int DB = G % ND;
+        constexpr int OFS = (T == 0 ? RB : 0) + J * 16 * D * 2;
+        u32x2 v[2];
+        v[0] = lds_read_tr<OFS>(zk[0][DB]);
+        v[1] = lds_read_tr<OFS>(zk[1][DB]);
+        return join_tr(v);
+      };
+      static_for<0, 2 * NS>([&](auto m_c) {
+        constexpr int M = decltype(m_c)::value;
+        constexpr int FA = M + LA;
+        if constexpr (FA < NS)
+          cur[FA] = read_x(rk, IC<FA>{});
+        else if constexpr (FA < 2 * NS)
+          cur[FA] = read_z(IC<FA>{});
+        else
+          pre[FA - 2 * NS] = read_x(rn, IC<FA - 2 * NS>{});
+        if constexpr (M == SLR)
+          static_for<0, 4>([&](auto j_c) { lv[j_c] = lds_read_f32x4<32 * j_c>(la); });
+        if constexpr (M == SDR)
+          static_for<0, 4>([&](auto j_c) { dl[j_c] = lds_read_f32x4<128 + 32 * j_c>(la); });
+        lgkm_wait<sched.wait[M]>();
+        if constexpr (M == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tie(dl[j]);
+        }
+        if constexpr (M == NS) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tie(lv[j]);
+        }
+        bf16x8 a;
+        if constexpr (M < LA)
+          a = pre[M];
+        else
+          a = cur[M];
+        if constexpr (M < NS) {
+          // X(k): the S and dP chains alternate.
+          constexpr int S = M / 2;
+          if constexpr (M % 2 == 0) {
+            if constexpr (S == 0)
+              mfma_new(sc, a, kf[0]);
+            else
+              mfma_acc(sc, a, kf[S]);
+          } else {
+            if constexpr (S == 0)
+              mfma_new(dp[P], a, vf[0]);
+            else
+              mfma_acc(dp[P], a, vf[S]);
+          }
+          // Block k-1: dS of EPS elements, and the bf16 packing of P (masked
+          // at the end of the previous iteration) and of dS.
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int r = EPS * M + e;
+            const float y = acc_read(dp[P ^ 1][r]);
+            dsv[r] = pv[r] * (y - dl[r >> 2][r & 3]);
+          }
+          if constexpr ((EPS * M + EPS - 1) % 2 == 1) {
+            constexpr int W = (EPS * M + EPS - 1) / 2;
+            sw[W] = __builtin_bit_cast(uint32_t, to_bf16x2(dsv[2 * W], dsv[2 * W + 1]));
+            tie(sw[W]);
+          }
+          if constexpr (M < 8) {
+            pw[M] = __builtin_bit_cast(uint32_t, to_bf16x2(pv[2 * M], pv[2 * M + 1]));
+            tie(pw[M]);
+          }
+          if constexpr (M == NS - 1) {
+            // Every wavefront's copies of block k+1 have landed and nobody
+            // reads the stage of block k-2 any more: refill it with block k+3.
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm<NV>());
+            asm volatile("s_barrier" ::: "memory");
+            asm volatile("" : "+s"(lb));
+            walk_to(cw, k + 3);
+            int st3 = next_st(stn);
+            st3 = next_st(st3);
+            copy_block(plane0 + cw.h, qs + 32 * cw.i, st3);
+          }
+        } else {
+          // Z(k-1) with block k-1's P and dS, and P of EPS elements of block k.
+          constexpr int G = M - NS;
+          constexpr int T = G / (2 * ND);
+          constexpr int J = (G / ND) % 2;
+          constexpr int DB = G % ND;
+          bf16x8 bop;
+          const u32x4 wq = T == 0 ? u32x4{pw[4 * J], pw[4 * J + 1], pw[4 * J + 2], pw[4 * J + 3]}
+                                  : u32x4{sw[4 * J], sw[4 * J + 1], sw[4 * J + 2], sw[4 * J + 3]};
+          __builtin_memcpy(&bop, &wq, sizeof(wq));
+          if constexpr (T == 0)
+            mfma_acc(dv[DB], a, bop);
+          else
+            mfma_acc(dk[DB], a, bop);
+#pragma unroll
+          for (int e = 0; e < EPS; ++e) {
+            const int r = EPS * G + e;
+            const float x = acc_read(sc[r]);
+            pv[r] = exp2_fast(fmaf(x, c, -lv[r >> 2][r & 3]));
+            tie(pv[r]);
+          }
+        }
+      });
+      if (ymask) {
+        // Row offsets 8*(r/4) + r%4 outside [lo, hi) are masked: rows past Tq
+        // (or all, off this workgroup's blocks), and under the causal mask
+        // rows before this lane's key.
+        const int base = qy + 4 * half;
+        const int lo = CAUSAL ? my_k - off - base : -64;
+        const int hi = yvalid ? p.Tq - base : -64;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = 8 * (r >> 2) + (r & 3);
+          pv[r] = (o >= lo && o < hi) ? pv[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NC; ++s) rk[s] = rn[s];
+      st = stn;
+    };
+    for (int k = kbeg; k < kbeg + niter; k += 2) {
+      iteration(k, IC<0>{});
+      iteration(k + 1, IC<1>{});
+    }
+    // Copies and reads issued for iterations that do not run.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    lgkm_wait<0>();
   }
+
+  // No accumulator is read within 24 wait states of its last product.
+#pragma unroll
+  for (int db = 0; db < ND; ++db) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dv[db]), "+a"(dk[db]));
 
   if (my_k < p.Tk) {
     if (p.kparts == 1) {
