@@ -18,9 +18,12 @@
 // inputs up to the rounding stated here: q.k products of 8-bit values are
 // exact and summed in fp32 on the matrix core (32x32x64 8-bit MFMA); the
 // online softmax runs in fp32 as in the bf16 kernel; the probabilities are
-// rounded to E4M3 for the P.V product (P times 448, so that the largest
-// probability of a row, exactly 1, maps to the largest code), which is the
-// one rounding step that the 16-bit kernel does in bf16.
+// rounded to E4M3 for the P.V product, which is the one rounding step that
+// the 16-bit kernel does in bf16.  They are scaled by 448 * 2^-kF8Headroom
+// against a lazily moved reference max (see kF8Headroom), so the largest
+// probability of a row lands between 224 and 448, within the largest code;
+// codes below the normal range carry an absolute error of at most 2^-10,
+// i.e. 2^(kF8Headroom-10) / 448 in probability units.
 //
 // Mapping onto CDNA4 (the bf16 kernel's design with 8-bit operands):
 //  * 512 threads = 8 wavefronts of 32 query rows; HG query heads of a GQA
@@ -49,6 +52,12 @@ constexpr int kF8Threads = 512;
 constexpr int kF8Stages = 4;
 constexpr int kF8BN = 64;                  // keys per tile
 constexpr float kLog2E4M3Max = 8.807354922057604f;   // log2(448)
+// Bits of probability between a row's reference max and the largest E4M3
+// value: probabilities are taken as 448 * 2^-kF8Headroom * 2^((s - m) cq)
+// against a reference m that moves only when a tile's max exceeds it by more
+// than kF8Headroom bits, so they never pass 448 and the accumulator is
+// rescaled only on such moves.
+constexpr float kF8Headroom = 1.f;
 
 // Byte tiles (rows x D codes, row-major): 16-byte chunk c of row r sits at
 // position c ^ f8swz(r).  The function depends only on row bits that
@@ -249,9 +258,11 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       qf[c] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
                     (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
     }
-    // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks.
+    // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks, and
+    // the headroom in raw product units.
     const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
     const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
+    const float hr = kF8Headroom / cq;
 
     const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
     const int ntiles = (kend + BN - 1) / BN;
@@ -262,7 +273,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
     // has shown it no key yet.
     const bool has_keys = !CAUSAL || my_q + off >= 0;
 
-    float m = kNegInf;   // running max of this row's raw 8-bit products
+    float m = kNegInf;   // reference max of this row's raw 8-bit products
     float l = 0.f;       // this half-wave's share of the running sum of 448 * P
     f32x16 acc[ND];
 #pragma unroll
@@ -328,7 +339,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       for (int i = 2; i < 32; i += 2)
         mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
       mt = max_halves8(mt);
-      const float m_new = fmaxf(m, mt);
+      const float m_new = mt > m + hr ? mt : m;
       const bool live = KSPLIT ? m_new > kNegInf : has_keys;
       const float corr = live ? exp2_fast((m - m_new) * cq) : 1.f;
       if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
@@ -337,9 +348,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       }
       l *= corr;
       m = m_new;
-      // 448 * P = 2^(s*cq - m*cq + log2 448): the row's largest probability
-      // becomes the largest E4M3 value.
-      const float mc = live ? m * cq - kLog2E4M3Max : 0.f;
+      // 448 * 2^-headroom * P = 2^(s*cq - m*cq + log2 448 - headroom).
+      const float mc = live ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -422,8 +432,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       tile_barrier();   // the exchange slots are free before the next pass's copies
     }
 
-    // O = acc * vs / l (the 448 of the probabilities cancels); lse in natural
-    // log: (m*cq + log2(l) - log2 448) * ln 2.
+    // O = acc * vs / l (the 448 * 2^-headroom of the probabilities cancels);
+    // lse in natural log: (m*cq + log2(l) - log2 448 + headroom) * ln 2.
     const float lt = sum_halves8(l);
     const float inv = lt > 0.f ? vs / lt : 0.f;
     if (active && kh == 0 && my_q < p.Tq) {
@@ -438,7 +448,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         }
       if (p.lse != nullptr && half == 0)
         p.lse[qplane * p.Tq + my_q] =
-            lt > 0.f ? (m * cq + __builtin_amdgcn_logf(lt) - kLog2E4M3Max) * kLn2 : kNegInf;
+            lt > 0.f ? (m * cq + __builtin_amdgcn_logf(lt) - kLog2E4M3Max + kF8Headroom) * kLn2 : kNegInf;
     }
   }
 }

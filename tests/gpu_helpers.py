@@ -193,17 +193,22 @@ def check_bounded(name, got, want, bound):
 # 8-bit forward: element-wise error bound
 # ---------------------------------------------------------------------------
 E4M3_U = 2.0 ** -4            # relative rounding of an E4M3 normal value (3 mantissa bits)
-E4M3_FLOOR = 2.0 ** -10 / 448  # absolute rounding of 448 * P below the smallest normal, in P units
+F8_HEADROOM = 1                # bits between a row's reference max and the largest E4M3 code
+# Absolute rounding of a probability code below the smallest normal, in P
+# units: the kernel codes 448 * 2^-F8_HEADROOM * P against a reference at
+# most the row's max, and a subnormal code rounds by at most 2^-10.
+E4M3_FLOOR = 2.0 ** (F8_HEADROOM - 10) / 448
 
 
 def fp8_fwd_error_bound(q, k, v, *, causal, scale, causal_off=0, safety=1.25):
     """Bound on |O_kernel - O_exact| for fa_fwd_fp8, element by element.
 
     q, k, v: the dequantised fp64 inputs.  The only rounding of consequence
-    is that of each probability P_ij = exp(s_ij - m_i) <= 1 (times 448) to
-    E4M3 before the P.V product: |dP| <= max(2^-4 P, 2^-10/448).  With the
-    row sum l_i = sum_j P_ij unrounded,
-        |O_err[i, c]| <= sum_j max(2^-4 P_ij, 2^-10/448) |v_jc| / l_i,
+    is that of each probability P_ij = exp(s_ij - m_i) <= 1 (coded as 448 *
+    2^-F8_HEADROOM * P against a reference at most m_i) to E4M3 before the P.V
+    product: |dP| <= max(2^-4 P, E4M3_FLOOR).  With the row sum
+    l_i = sum_j P_ij unrounded,
+        |O_err[i, c]| <= sum_j max(2^-4 P_ij, E4M3_FLOOR) |v_jc| / l_i,
     plus the bf16 rounding of O (2^-8 |O|); times `safety`, plus 1e-6."""
     B, Hq, Tq, d = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
