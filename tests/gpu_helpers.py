@@ -190,6 +190,49 @@ def check_bounded(name, got, want, bound):
 
 
 # ---------------------------------------------------------------------------
+# Decode: element-wise error bound
+# ---------------------------------------------------------------------------
+def decode_error_bound(q, K, V, seqlens, *, safety=1.25):
+    """Bound on |O_kernel - O_exact| for fa_decode (bf16 cache) and
+    fa_decode_fp8 / fa_decode_int8 (8-bit codes with per-row scales), element
+    by element.
+
+    q: [B, Hq, d] fp64 queries; K, V: [B, Hkv, Tmax, d] fp64 cache rows as
+    the oracle reads them (dequantised; only each sequence's valid prefix is
+    used).  The kernels form scores from exact bf16 products with fp32 sums,
+    P_j = 2^(s_j c - m c) in fp32, the row sum l from the unrounded P, and
+    round P_j (times the V row scale, for 8-bit caches) to bf16 before the
+    P.V product, which sums in fp32; partial results merge by the rescale
+    rule in fp32 and O is rounded to bf16.  So, with A = sum_j P_j |v_j| / l:
+      * rounding P to bf16: at most 2^-8 A;
+      * rounding O to bf16: at most 2^-8 |O|;
+      * the fp32 score and exponent error, a relative error ds of every P_j:
+        at most ds (A + |O|), ds = (d + 4) 2^-24 |scale| max_j sum_i |q_i k_ji|
+        + 2^-21;
+    plus the fp32 sums (n 2^-24 relative, absorbed by `safety`) and 1e-6."""
+    B, Hq, d = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    scale = 1.0 / np.sqrt(d)
+    out = np.full((B, Hq, V.shape[3]), 1e-6)
+    for b in range(B):
+        n = int(seqlens[b])
+        if n == 0:
+            continue
+        for h in range(Hq):
+            k = K[b, h // g, :n]
+            v = V[b, h // g, :n]
+            s = scale * (k @ q[b, h])
+            P = np.exp(s - s.max())
+            l = P.sum()
+            A = (P @ np.abs(v)) / l
+            O = (P @ v) / l
+            ds = (d + 4) * 2.0 ** -24 * scale * float(np.max(np.abs(k) @ np.abs(q[b, h]))) + 2.0 ** -21
+            out[b, h] = safety * (2.0 ** -8 + ds) * (A + np.abs(O)) + 1e-6
+    return out
+
+
+# ---------------------------------------------------------------------------
 # 8-bit forward: element-wise error bound
 # ---------------------------------------------------------------------------
 E4M3_U = 2.0 ** -4            # relative rounding of an E4M3 normal value (3 mantissa bits)

@@ -1,5 +1,8 @@
 """GPU parity of split-KV flash-decoding (fa_decode) against the fp64 CPU
-oracle, through the C ABI.  Bar: |O err| <= 1.5e-2 (bf16 inputs)."""
+oracle, through the C ABI.  Bar: every output element within
+gpu_helpers.decode_error_bound, derived from the kernel's arithmetic (bf16
+rounding of P and of O, fp32 scores and sums); two kernel results of the
+same inputs differ by at most twice that bound."""
 import math
 
 import numpy as np
@@ -7,7 +10,8 @@ import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import BF16_O_TOL, check, dev_bf16, host_bf16_as_f64, max_err, say
+from gpu_helpers import (check_bounded, decode_error_bound, dev_bf16, host_bf16_as_f64, max_err,
+                         say)
 
 pytestmark = pytest.mark.gpu
 
@@ -20,6 +24,10 @@ def _gpu():
         pytest.skip("no GPU")
     from exact_tiled_attention_02_amd import fa
     fa.load()
+
+
+def bound_of(q, kc, vc, sl):
+    return decode_error_bound(oracle.as_f64(q), oracle.as_f64(kc), oracle.as_f64(vc), sl)
 
 
 def run_decode(q, kc, vc, seqlens, num_splits):
@@ -60,7 +68,7 @@ def test_decode_small(case, num_splits):
     say("fa_decode", case, "splits", num_splits)
     O = run_decode(q, kc, vc, sl, num_splits)
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound_of(q, kc, vc, sl))
     for b, n in enumerate(sl):
         if n == 0:
             assert np.all(O[b] == 0)
@@ -72,17 +80,17 @@ def flash_decode_case():
     say("generating", w.name)
     q, kc, vc, sl = inputs.decode_inputs(w, poison_tail=True)
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
-    return q, kc, vc, sl, Or
+    return q, kc, vc, sl, Or, bound_of(q, kc, vc, sl)
 
 
 @pytest.mark.parametrize("num_splits", [0, 1, 8, 16, 32, 64])
 def test_flash_decode_workload_full(flash_decode_case, num_splits):
     """B=16, Hq=32, Hkv=8, d=128, seqlens U[1024, 32768] (seed 0), cache
     poisoned with NaN past every valid prefix; every output element."""
-    q, kc, vc, sl, Or = flash_decode_case
+    q, kc, vc, sl, Or, bound = flash_decode_case
     say("fa_decode", inputs.FLASH_DECODE.name, "splits", num_splits)
     O = run_decode(q, kc, vc, sl, num_splits)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound)
 
 
 def test_decode_deterministic_and_split_independent():
@@ -93,7 +101,7 @@ def test_decode_deterministic_and_split_independent():
     b = run_decode(q, kc, vc, sl, 5)
     assert np.array_equal(a, b)
     c = run_decode(q, kc, vc, sl, 31)
-    check("O", a, c, BF16_O_TOL)
+    check_bounded("O", a, c, 2 * bound_of(q, kc, vc, sl))
 
 
 def test_decode_equals_single_row_forward():
@@ -103,6 +111,7 @@ def test_decode_equals_single_row_forward():
     q, kc, vc, sl = inputs.decode_inputs(w)
     say("fa_decode vs fa_fwd")
     O = run_decode(q, kc, vc, sl, 4)
+    bound = bound_of(q, kc, vc, sl)
     for b in range(3):
         n = int(sl[b])
         tq = dev_bf16(q[b:b + 1, :, None, :])
@@ -111,7 +120,7 @@ def test_decode_equals_single_row_forward():
         o = torch.empty(1, 8, 1, 128, dtype=torch.bfloat16, device="cuda")
         fa.fa_fwd(tq, tk, tv, o, None, 1, 8, 2, 1, n, 128, False, 1 / math.sqrt(128))
         torch.cuda.synchronize()
-        check("O", O[b], host_bf16_as_f64(o)[0, :, 0], BF16_O_TOL)
+        check_bounded("O", O[b], host_bf16_as_f64(o)[0, :, 0], 2 * bound[b])
 
 
 def test_automatic_workgroup_count_fills_the_device():
@@ -134,7 +143,7 @@ def test_decode_many_ranges_per_sequence(num_splits):
     say("fa_decode many ranges", num_splits)
     O = run_decode(q, kc, vc, sl, num_splits)
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound_of(q, kc, vc, sl))
 
 
 def test_workspace_reuse_across_shapes():
@@ -149,7 +158,7 @@ def test_workspace_reuse_across_shapes():
         say("fa_decode reuse", B, Tmax)
         O = run_decode(q, kc, vc, sl, 0 if i % 2 else 37)
         Or, _ = oracle.decode_attention(q, kc, vc, sl)
-        check("O", O, Or, BF16_O_TOL)
+        check_bounded("O", O, Or, bound_of(q, kc, vc, sl))
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096, (1 << 20) + 48, 3 * (1 << 20)])

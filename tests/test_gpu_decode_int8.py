@@ -1,14 +1,15 @@
 """GPU parity of decode over an int8 KV cache (fa_decode_int8: two's-complement
 codes, one fp32 scale per row, dequantised in the kernel) against the fp64
-oracle, through the C ABI.  Bar: |O err| <= 1.5e-2 (the bf16 decode bar:
-every int8 value widens exactly to bf16 and the arithmetic is the bf16
-decode's)."""
+oracle, through the C ABI.  Bar: every output element within
+gpu_helpers.decode_error_bound of the dequantised cache (the bf16 decode's
+bound: every int8 value widens exactly to bf16 and the arithmetic is the bf16
+decode's, the V row scale applied to P before its bf16 rounding)."""
 import numpy as np
 import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import BF16_O_TOL, check, dev_bf16, host_bf16_as_f64, say
+from gpu_helpers import check_bounded, decode_error_bound, dev_bf16, host_bf16_as_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +22,13 @@ def _gpu():
         pytest.skip("no GPU")
     from exact_tiled_attention_02_amd import fa
     fa.load()
+
+
+def bound_of(q, kc, vc, ks, vs, sl):
+    """decode_error_bound on the dequantised cache rows."""
+    K = oracle.int8_to_f64(kc) * np.asarray(ks, np.float64)[..., None]
+    V = oracle.int8_to_f64(vc) * np.asarray(vs, np.float64)[..., None]
+    return decode_error_bound(oracle.as_f64(q), K, V, sl)
 
 
 def run_decode_int8(q, kc, vc, ks, vs, seqlens, num_splits):
@@ -71,7 +79,7 @@ def test_decode_int8_small(case, num_splits):
     say("fa_decode_int8", case, "splits", num_splits)
     O = run_decode_int8(q, kc, vc, ks, vs, sl, num_splits)
     Or, _ = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound_of(q, kc, vc, ks, vs, sl))
     for b, n in enumerate(sl):
         if n == 0:
             assert np.all(O[b] == 0)
@@ -94,7 +102,7 @@ def test_decode_int8_every_code():
     say("fa_decode_int8 all codes")
     O = run_decode_int8(q, kc, vc, ks, vs, sl, 3)
     Or, _ = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound_of(q, kc, vc, ks, vs, sl))
 
 
 @pytest.fixture(scope="module")
@@ -103,17 +111,17 @@ def flash_decode_int8_case():
     say("generating", w.name)
     q, kc, vc, ks, vs, sl = inputs.decode_inputs_int8(w, poison_tail=True)
     Or, _ = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
-    return q, kc, vc, ks, vs, sl, Or
+    return q, kc, vc, ks, vs, sl, Or, bound_of(q, kc, vc, ks, vs, sl)
 
 
 @pytest.mark.parametrize("num_splits", [0, 64])
 def test_flash_decode_int8_workload_full(flash_decode_int8_case, num_splits):
     """B=16, Hq=32, Hkv=8, d=128, seqlens U[1024, 32768] (seed 0), int8 cache
     with per-row scales, code -128 past every valid prefix; every output."""
-    q, kc, vc, ks, vs, sl, Or = flash_decode_int8_case
+    q, kc, vc, ks, vs, sl, Or, bound = flash_decode_int8_case
     say("fa_decode_int8", inputs.FLASH_DECODE_INT8.name, "splits", num_splits)
     O = run_decode_int8(q, kc, vc, ks, vs, sl, num_splits)
-    check("O", O, Or, BF16_O_TOL)
+    check_bounded("O", O, Or, bound)
 
 
 def test_decode_int8_deterministic():
@@ -150,5 +158,6 @@ def test_decode_int8_matches_bf16_decode_of_widened_cache():
     torch.cuda.synchronize()
     Ob = host_bf16_as_f64(o)
     Or, _ = oracle.decode_attention_int8(q, kc, vc, ks, vs, sl)
-    check("O int8 vs oracle", O8, Or, BF16_O_TOL)
-    check("O int8 vs bf16 decode", O8, Ob, BF16_O_TOL)
+    bound = bound_of(q, kc, vc, ks, vs, sl)
+    check_bounded("O int8 vs oracle", O8, Or, bound)
+    check_bounded("O int8 vs bf16 decode", O8, Ob, 2 * bound)

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from exact_tiled_attention_02_amd import inputs
-from gpu_helpers import BF16_O_TOL, check, dev_bf16, host_bf16_as_f64, say
+from gpu_helpers import check_bounded, decode_error_bound, dev_bf16, host_bf16_as_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,8 @@ def test_noalloc_matches_decode_on_two_calls(num_splits):
         b = o_na.view(torch.int16).cpu().numpy()
         assert np.array_equal(a, b), "fa_decode_noalloc differs from fa_decode"
         Or, _ = oracle.decode_attention(q, kc, vc, sl)
-        check("O", host_bf16_as_f64(o_na), Or, BF16_O_TOL)
+        check_bounded("O", host_bf16_as_f64(o_na), Or,
+                      decode_error_bound(oracle.as_f64(q), oracle.as_f64(kc), oracle.as_f64(vc), sl))
         assert np.all(host_bf16_as_f64(o_na)[0] == 0)
 
 
@@ -85,4 +86,5 @@ def test_noalloc_refuses_oversized_workspace():
     fa.fa_decode(tq, tk, tv, tsl, o, B, Hq, Hkv, Tmax, d, splits, torch.cuda.current_stream())
     torch.cuda.synchronize()
     Or, _ = oracle.decode_attention(q, kc, vc, sl)
-    check("O", host_bf16_as_f64(o), Or, BF16_O_TOL)
+    check_bounded("O", host_bf16_as_f64(o), Or,
+                  decode_error_bound(oracle.as_f64(q), oracle.as_f64(kc), oracle.as_f64(vc), sl))
