@@ -389,10 +389,136 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         acc[db] = mma_f8(a, pb, acc[db]);
       }
     };
-    for (int t = 0; t < ntiles; t += STAGES) {
-      static_for<0, STAGES>([&](auto s_c) {
-        if (t + decltype(s_c)::value < ntiles) tile(t + decltype(s_c)::value, s_c);
-      });
+    if constexpr (KSPLIT || D != 128) {
+      // (At d = 64 the pipelined loop's second score set would take the
+      // kernel from 115 to 148 registers, one workgroup per CU instead of two.)
+      for (int t = 0; t < ntiles; t += STAGES) {
+        static_for<0, STAGES>([&](auto s_c) {
+          if (t + decltype(s_c)::value < ntiles) tile(t + decltype(s_c)::value, s_c);
+        });
+      }
+    } else {
+      // Software-pipelined tile loop (d = 128, no key split): tile t+1's
+      // scores go to the matrix core before tile t's exponentials and
+      // packing, and tile t+1's mask and max follow tile t's P.V, so every
+      // phase of VALU work has independent matrix-core work beside it in the
+      // same wavefront.  Tile t+1 must have landed at tile t's barrier:
+      // copies run two tiles ahead of it.
+      f32x16 sbuf[2][2];                   // scores of tiles t (even/odd) and t+1
+      float m_next = m, corr_next = 1.f;   // the reference move due at tile t+1
+      bool move_next = false;
+      auto scores = [&](auto st_c, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        constexpr int KT = decltype(st_c)::value * TILE;
+        u32x4 kr[2][2 * NC8];
+        static_for<0, 2 * NC8>([&](auto i_c) {
+          kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
+          kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
+        });
+        lgkm_wait<0>();
+#pragma unroll
+        for (int i = 0; i < 2 * NC8; ++i) {
+          tie(kr[0][i]);
+          tie(kr[1][i]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[kb] = f32x16{};
+#pragma unroll
+          for (int c = 0; c < NC8; ++c) {
+            const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
+            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            s[kb] = mma_f8(a, qf[c], s[kb]);
+          }
+        }
+      };
+      // Mask tile t's scores, take its max and decide the reference move.
+      // Tiles past this wavefront's last (formed on stale stage data) are
+      // masked whole and move nothing.
+      auto decide = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const int t0 = t * BN;
+        const bool need_mask = (t0 + 64 > p.Tk) || (CAUSAL && t0 + 63 > q0w + off);
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+              const bool vis = key < p.Tk && (!CAUSAL || key <= my_q + off);
+              s[kb][r] = vis ? s[kb][r] : kNegInf;
+            }
+        }
+        float mt = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+        for (int i = 2; i < 32; i += 2)
+          mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
+        mt = max_halves8(mt);
+        m_next = mt > m + hr ? mt : m;
+        corr_next = has_keys ? exp2_fast((m - m_next) * cq) : 1.f;
+        move_next = __builtin_amdgcn_ballot_w64(m_next > m) != 0;
+      };
+      auto step = [&](int t, auto st_c) __attribute__((always_inline)) {
+        constexpr int ST = decltype(st_c)::value;
+        constexpr int VT = ST * TILE;   // vread already points at the V stages
+        constexpr int CUR = ST & 1;
+        wait_copies(ntiles - 2 - t >= 1 ? 1 : 0);
+        tile_barrier();
+        if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
+        if (t >= my_tiles) return;
+        if (move_next) {
+#pragma unroll
+          for (int i = 0; i < ND; ++i) acc[i] *= corr_next;
+        }
+        l *= corr_next;
+        m = m_next;
+        scores(IC<(ST + 1) % STAGES>{}, sbuf[CUR ^ 1]);
+        u32x2 va[ND][4];
+        static_for<0, ND>([&](auto db_c) {
+          static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
+        });
+        // 448 * 2^-headroom * P = 2^(s*cq - m*cq + log2 448 - headroom).
+        const float mc = has_keys ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
+        f32x16 (&s)[2] = sbuf[CUR];
+        float ls[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
+            ls[r & 3] = kb == 0 && r < 4 ? s[kb][r] : ls[r & 3] + s[kb][r];
+          }
+        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        i32x8 pb;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int kb = w >> 2, r = 4 * (w & 3);
+          pb[w] = pack_e4m3x4(s[kb][r], s[kb][r + 1], s[kb][r + 2], s[kb][r + 3]);
+        }
+        lgkm_wait<0>();
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) tie(va[db][j]);
+          const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
+                           (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
+          acc[db] = mma_f8(a, pb, acc[db]);
+        }
+        decide(t + 1, sbuf[CUR ^ 1]);
+      };
+      // Tile 0's scores, mask and max.
+      if (ntiles > 0) {
+        wait_copies(min(ntiles - 1, STAGES - 2));
+        tile_barrier();
+        if (my_tiles > 0) {
+          scores(IC<0>{}, sbuf[0]);
+          decide(0, sbuf[0]);
+        }
+      }
+      for (int t = 0; t < ntiles; t += STAGES) {
+        static_for<0, STAGES>([&](auto s_c) {
+          if (t + decltype(s_c)::value < ntiles) step(t + decltype(s_c)::value, s_c);
+        });
+      }
     }
 
     if constexpr (KSPLIT) {
