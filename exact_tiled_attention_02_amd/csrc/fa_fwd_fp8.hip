@@ -103,7 +103,10 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
   // every 128-key tile, in two passes (heavy half-tile, then light), and
   // merge their (m, l, acc) at the end of each pass.
   constexpr int BN = KSPLIT ? 2 * kF8BN : kF8BN;            // keys per tile
-  constexpr int STAGES = KSPLIT ? kF8Stages / 2 : kF8Stages;
+  // Under the key split at d = 64 (the plain loop) two stages of 128-key
+  // tiles; otherwise four, so that the pipelined loop below finds tile t+1
+  // landed at tile t's barrier with tile t+2 still in flight.
+  constexpr int STAGES = KSPLIT && D != 128 ? kF8Stages / 2 : kF8Stages;
   constexpr int RPH = KSPLIT ? WPH / 2 : WPH;               // 32-row blocks per query head
   constexpr int NPASS = KSPLIT ? 2 : 1;
   constexpr int TILE = BN * D;           // bytes of one K or V tile
@@ -114,7 +117,9 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
   constexpr int CWW = CW < NW ? CW : NW; // wavefronts that copy
   constexpr int NCP = CW / CWW;          // copies per copying wavefront, tile and tensor
   static_assert(CW >= 1 && CW % CWW == 0, "tile size and workgroup do not match");
-  static_assert((2 * STAGES - 1) * TILE + 48 * D < 65536, "operand offsets must fit the immediate");
+  // K reads add up to (STAGES-1)*TILE + 32*D to their base, V reads (whose
+  // base already points at the V stages) up to (STAGES-1)*TILE + 48*D.
+  static_assert((STAGES - 1) * TILE + 48 * D < 65536, "operand offsets must fit the immediate");
   // Key split: the merge hands (m, l) and the accumulator of NW/2 row blocks
   // over through LDS, one 16-byte vector per lane and slot.
   constexpr int XCH = KSPLIT ? (NW / 2) * (4 * ND + 1) * 64 * 16 : 0;
@@ -389,7 +394,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         acc[db] = mma_f8(a, pb, acc[db]);
       }
     };
-    if constexpr (KSPLIT || D != 128) {
+    if constexpr (D != 128) {
       // (At d = 64 the pipelined loop's second score set would take the
       // kernel from 115 to 148 registers, one workgroup per CU instead of two.)
       for (int t = 0; t < ntiles; t += STAGES) {
@@ -398,7 +403,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         });
       }
     } else {
-      // Software-pipelined tile loop (d = 128, no key split): tile t+1's
+      // Software-pipelined tile loop (d = 128): tile t+1's
       // scores go to the matrix core before tile t's exponentials and
       // packing, and tile t+1's mask and max follow tile t's P.V, so every
       // phase of VALU work has independent matrix-core work beside it in the
@@ -436,7 +441,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       // Tiles past this wavefront's last (formed on stale stage data) are
       // masked whole and move nothing.
       auto decide = [&](int t, f32x16 (&s)[2]) __attribute__((always_inline)) {
-        const int t0 = t * BN;
+        const int t0 = t * BN + 64 * kh;   // this wavefront's first key
         const bool need_mask = (t0 + 64 > p.Tk) || (CAUSAL && t0 + 63 > q0w + off);
         if (need_mask) {
 #pragma unroll
@@ -454,14 +459,18 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
           mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
         mt = max_halves8(mt);
         m_next = mt > m + hr ? mt : m;
-        corr_next = has_keys ? exp2_fast((m - m_next) * cq) : 1.f;
+        // Under the key split a row whose key half has shown it no key yet
+        // stays at m = -inf, factor 1 and offset 0, tile by tile.
+        const bool live = KSPLIT ? m_next > kNegInf : has_keys;
+        corr_next = live ? exp2_fast((m - m_next) * cq) : 1.f;
         move_next = __builtin_amdgcn_ballot_w64(m_next > m) != 0;
       };
       auto step = [&](int t, auto st_c) __attribute__((always_inline)) {
         constexpr int ST = decltype(st_c)::value;
         constexpr int VT = ST * TILE;   // vread already points at the V stages
         constexpr int CUR = ST & 1;
-        wait_copies(ntiles - 2 - t >= 1 ? 1 : 0);
+        // Issued so far: tiles up to t + STAGES - 2; tile t+1 must be in.
+        wait_copies(max(0, min(ntiles - 2 - t, STAGES - 3)));
         tile_barrier();
         if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
         if (t >= my_tiles) return;
@@ -477,7 +486,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
           static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
         });
         // 448 * 2^-headroom * P = 2^(s*cq - m*cq + log2 448 - headroom).
-        const float mc = has_keys ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
+        const bool live = KSPLIT ? m > kNegInf : has_keys;
+        const float mc = live ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
         f32x16 (&s)[2] = sbuf[CUR];
         float ls[4];
 #pragma unroll
@@ -524,8 +534,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
     if constexpr (KSPLIT) {
       // The two key halves of the same rows combine by the rescale rule:
       // the second-half wavefront hands its (m, l, acc) over through LDS (one
-      // 16-byte vector per lane and slot).  No copy is in flight: with two
-      // stages every tile waits for all copies issued before it.
+      // 16-byte vector per lane and slot).  No copy is in flight: the last
+      // tile of a pass waits for every copy issued before it.
       tile_barrier();
       f32x4* xch = (f32x4*)lds + rw * (4 * ND + 1) * 64 + lane;
       if (kh == 1) {
