@@ -14,7 +14,7 @@
 // unnormalised output accumulator; when the reference max moves the old l
 // and accumulator are multiplied by 2^((ref_old - ref_new) * c).  The bf16
 // kernel moves its reference only when a row's max has outgrown it by more
-// than a factor 2^8 and undoes the bf16 rounding of the largest probability
+// than a factor 2^16 and undoes the bf16 rounding of the largest probability
 // (top_fix), which keeps the exact-max result.  O = acc / l is written once
 // at the end together with lse = ref + log l.  Neither scores nor
 // probabilities ever leave the chip.
@@ -118,7 +118,10 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 // Lazy reference of the bf16 kernel: the accumulator is rescaled only when a
 // row's max has grown past its reference by more than this many powers of 2.
-constexpr float kLazyLog2 = 8.f;
+// fp32 and bf16 have the same relative precision at any magnitude, so the
+// bound only keeps the sums far from overflow: probabilities stay below
+// 2^16, row sums below 2^16 per key.
+constexpr float kLazyLog2 = 16.f;
 
 // x / bf16(x).  The accumulator holds bf16-rounded probabilities times V
 // while l sums them unrounded, so a row dominated by one key would come out
@@ -163,6 +166,9 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   constexpr int NCOPY = TILE / 8 / kFwdThreads;   // 16-byte copies per thread per tile and tensor
   static_assert(NCOPY >= 1 && TILE / 8 % kFwdThreads == 0, "tile does not split over the workgroup");
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * STAGES * TILE];   // K stages | V stages
+  // Key split: (m, reference, l) of the second key half, handed over at the
+  // end of a pass.
+  __shared__ f32x4 xch_sc[KSPLIT ? (NW / 2) * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,13 +205,19 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
   //      w+4) get one light and one heavy block.
   int q0w = 0, q_end = 0;
   bool active = true;  // false: nothing to compute in this pass
-  auto set_rows = [&](int pass) {
+  auto rows_of = [&](int pass, int& q0w, int& q_end, bool& active) {
     if constexpr (KSPLIT) {
       constexpr int HALF = BMPOS / 2;
       const int nh = (p.Tq + HALF - 1) / HALF;
       const int i = blockIdx.y;
-      const int ht = pass == 0 ? nh - 1 - i : i;
-      active = pass == 0 || ht != nh - 1 - i;
+      // Odd workgroups take the light half-tile first, so that the passes
+      // of different workgroups end at different times and the loads and
+      // stores between them do not all compete at once.
+      const bool light_first = i & 1;
+      const int first = light_first ? i : nh - 1 - i;
+      const int second = light_first ? nh - 1 - i : i;
+      const int ht = pass == 0 ? first : second;
+      active = pass == 0 || first != second;
       q0w = ht * HALF + (rw % RPH) * 32;
       q_end = min(p.Tq, (ht + 1) * HALF);
     } else if (CAUSAL && p.pair) {
@@ -225,6 +237,12 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     }
   };
   const int off = p.causal_off;   // causal: row i sees key j iff j <= i + off
+  // Key tiles a pass over rows ending before q_end needs: all, or under the
+  // causal mask those at or before its last (real) query row's limit.
+  auto tiles_of = [&](int q_end) {
+    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
+    return (kend + BN - 1) / BN;
+  };
 
   // Global->LDS copies through buffer resources covering this head's K and
   // V: reads past the last key return zeros (finite; those keys are masked).
@@ -296,28 +314,37 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
   const float c = p.c;
   const float lazy_raw = kLazyLog2 / c;
-  const uint32_t qsgn = p.negate_q ? 0x80008000u : 0u;
-
-  for (int pass = 0; pass < NPASS; ++pass) {
-    set_rows(pass);
-    if (KSPLIT && !active) break;   // the same for the whole workgroup
-    const int my_q = q0w + col;
-
-    // This lane's query row as the B operand of S^T = K Q^T:
-    // qf[c] = q[my_q][16c + 8*half .. +8].
-    bf16x8 qf[NC];
+  // This lane's query row as the B operand of S^T = K Q^T:
+  // qf[c] = q[row][16c + 8*half .. +8].  The sign flip (negative scale) sits
+  // behind a uniform branch so that, without it, nothing waits for the
+  // loads before the first product and the first key tile's copies are
+  // issued while they are in flight.
+  bf16x8 qf[NC];
+  auto load_q = [&](int row) {
+    u32x4 w[NC];
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (my_q < p.Tq) w = *(const u32x4*)(Qg + (size_t)my_q * D + 16 * cc + 8 * half);
-      w ^= qsgn;
-      __builtin_memcpy(&qf[cc], &w, sizeof(w));
+      w[cc] = u32x4{0u, 0u, 0u, 0u};
+      if (row < p.Tq) w[cc] = *(const u32x4*)(Qg + (size_t)row * D + 16 * cc + 8 * half);
     }
+    if (p.negate_q) {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) w[cc] ^= 0x80008000u;
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) __builtin_memcpy(&qf[cc], &w[cc], sizeof(w[cc]));
+  };
 
-    // Keys this workgroup needs: all, or under the causal mask those at or
-    // before its last (real) query row's limit.
-    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
-    const int ntiles = (kend + BN - 1) / BN;
+  // Key split: the next pass's query rows and first key tile are loaded
+  // while this pass's halves merge and its output is written.
+  bool prefetched = false;
+  for (int pass = 0; pass < NPASS; ++pass) {
+    rows_of(pass, q0w, q_end, active);
+    if (KSPLIT && !active) break;   // the same for the whole workgroup
+    const int my_q = q0w + col;
+    if (!prefetched) load_q(my_q);
+
+    const int ntiles = tiles_of(q_end);
     // Last tile this wavefront computes: its rows see none of its keys
     // after it.
     const int lim = q0w + 31 + off - 64 * kh;
@@ -338,7 +365,9 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
+    if (!prefetched)
+      for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
+    prefetched = false;
 
     // One key tile; ST = t % STAGES is a compile-time constant, so every
     // LDS operand address is a per-lane base plus an immediate offset.
@@ -415,8 +444,10 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
         const float corr = seen ? exp2_fast(nmc_new - nmc) : 0.f;
         const float fold = seen ? top_fix(exp2_fast(fmaf(m_prev, c, nmc))) : 1.f;
         const float f = corr * fold;
+        if (__builtin_amdgcn_ballot_w64(seen) != 0) {   // else acc is still 0
 #pragma unroll
-        for (int i = 0; i < ND; ++i) acc[i] *= f;
+          for (int i = 0; i < ND; ++i) acc[i] *= f;
+        }
         l *= corr;
         nmc = nmc_new;
         thr = m + lazy_raw;
@@ -504,20 +535,35 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       // the pass has been consumed and no copy is in flight (with two
       // stages each tile waits for all copies issued before it).
       tile_barrier();
-      static_assert((NW / 2) * (4 * ND + 1) * 64 * 16 <= (int)sizeof(lds), "exchange exceeds LDS");
-      f32x4* xch = (f32x4*)lds + rw * (4 * ND + 1) * 64 + lane;
+      // Stage 0 is free from here on: the next pass's query rows and first
+      // key tile start loading now.  The accumulators travel through the
+      // stage-1 K and V tiles, which the next pass fills only after its
+      // first tile's barrier, when every wavefront is past this exchange.
+      if (pass + 1 < NPASS) {
+        int nq0w = 0, nq_end = 0;
+        bool nactive = false;
+        rows_of(pass + 1, nq0w, nq_end, nactive);
+        if (nactive && tiles_of(nq_end) > 0) {
+          load_q(nq0w + col);
+          issue_copies(0);
+          prefetched = true;
+        }
+      }
+      static_assert(2 * 4 * ND * 64 * 16 <= TILE * 2, "exchange exceeds a stage-1 tile");
+      f32x4* xacc = (f32x4*)(lds + (rw < 2 ? 1 : STAGES + 1) * TILE) + (rw & 1) * 4 * ND * 64 + lane;
+      f32x4* xsc = xch_sc + rw * 64 + lane;
       if (kh == 1) {
-        xch[0] = f32x4{m, nmc, l, 0.f};
+        xsc[0] = f32x4{m, nmc, l, 0.f};
 #pragma unroll
         for (int db = 0; db < ND; ++db)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            xch[(1 + 4 * db + j) * 64] = f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2],
-                                               acc[db][4 * j + 3]};
+            xacc[(4 * db + j) * 64] = f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2],
+                                            acc[db][4 * j + 3]};
       }
       tile_barrier();
       if (kh == 0) {
-        const f32x4 o = xch[0];
+        const f32x4 o = xsc[0];
         const bool la = m > kNegInf, lb = o[0] > kNegInf;
         const float nmc_r = la && lb ? fminf(nmc, o[1]) : la ? nmc : o[1];
         const float fa = la ? exp2_fast(nmc_r - nmc) : 0.f;
@@ -529,12 +575,11 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
         for (int db = 0; db < ND; ++db)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const f32x4 o2 = xch[(1 + 4 * db + j) * 64];
+            const f32x4 o2 = xacc[(4 * db + j) * 64];
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[db][4 * j + e] = acc[db][4 * j + e] * fa + o2[e] * fb;
           }
       }
-      tile_barrier();   // the exchange slots are free before the next pass's copies
     }
 
     // Finalise: one division per row; lse in natural log.

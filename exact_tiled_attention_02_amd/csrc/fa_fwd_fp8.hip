@@ -240,37 +240,45 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
     }
   }
   const float vs = p.vscale[kvplane];
-  const uint32_t qsgn = p.negate_q ? 0x80808080u : 0u;
-
   for (int pass = 0; pass < NPASS; ++pass) {
     set_rows(pass);
     if (KSPLIT && !active) break;   // the same for the whole workgroup
     const int my_q = q0w + col;
 
+    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
+    const int ntiles = (kend + BN - 1) / BN;
+
     // This lane's query row as the B operand: 32 codes of head dimensions
-    // 64c + 32*half .. +32 (sign bits flipped for a negative scale).
-    i32x8 qf[NC8];
+    // 64c + 32*half .. +32 (sign bits flipped for a negative scale).  The
+    // first key tiles' copies are issued before anything waits for these
+    // loads; the sign flip sits behind a uniform branch for the same reason.
+    u32x4 qw[2 * NC8];
 #pragma unroll
     for (int c = 0; c < NC8; ++c) {
-      u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+      qw[2 * c] = u32x4{0u, 0u, 0u, 0u};
+      qw[2 * c + 1] = u32x4{0u, 0u, 0u, 0u};
       if (my_q < p.Tq) {
         const uint8_t* src = Qg + (size_t)my_q * D + 64 * c + 32 * half;
-        w0 = *(const u32x4*)src;
-        w1 = *(const u32x4*)(src + 16);
+        qw[2 * c] = *(const u32x4*)src;
+        qw[2 * c + 1] = *(const u32x4*)(src + 16);
       }
-      w0 ^= qsgn;
-      w1 ^= qsgn;
-      qf[c] = i32x8{(int)w0[0], (int)w0[1], (int)w0[2], (int)w0[3],
-                    (int)w1[0], (int)w1[1], (int)w1[2], (int)w1[3]};
     }
+    const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
+    for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
+    if (p.negate_q) {
+#pragma unroll
+      for (int c = 0; c < 2 * NC8; ++c) qw[c] ^= 0x80808080u;
+    }
+    i32x8 qf[NC8];
+#pragma unroll
+    for (int c = 0; c < NC8; ++c)
+      qf[c] = i32x8{(int)qw[2 * c][0], (int)qw[2 * c][1], (int)qw[2 * c][2], (int)qw[2 * c][3],
+                    (int)qw[2 * c + 1][0], (int)qw[2 * c + 1][1], (int)qw[2 * c + 1][2], (int)qw[2 * c + 1][3]};
     // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks, and
     // the headroom in raw product units.
-    const float qs = my_q < p.Tq ? p.qscale[qplane * p.Tq + my_q] : 1.f;
     const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
     const float hr = kF8Headroom / cq;
 
-    const int kend = CAUSAL ? max(0, min(p.Tk, q_end + off)) : p.Tk;
-    const int ntiles = (kend + BN - 1) / BN;
     const int lim = q0w + 31 + off - 64 * kh;   // last key its rows see, minus its block start
     const int my_tiles = !active ? 0 : CAUSAL ? (lim < 0 ? 0 : min(ntiles, lim / BN + 1)) : ntiles;
     // A row that sees no key keeps m = -inf, factor 1 and offset 0.  Under
@@ -285,8 +293,6 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
     for (int i = 0; i < ND; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-    for (int t = 0; t < min(ntiles, STAGES - 1); ++t) issue_copies(t);
 
     auto tile = [&](int t, auto st_c) __attribute__((always_inline)) {
       constexpr int ST = decltype(st_c)::value;
