@@ -16,14 +16,18 @@
 // scale (q_i = qs_i * e4m3(q8_i)), and each (batch, kv head) has one scale
 // for K and one for V.  The result is exact attention of those dequantised
 // inputs up to the rounding stated here: q.k products of 8-bit values are
-// exact and summed in fp32 on the matrix core (32x32x64 8-bit MFMA); the
-// online softmax runs in fp32 as in the bf16 kernel; the probabilities are
+// exact; the matrix core (32x32x64 8-bit MFMA) adds the 64 of a block with
+// terms far below the block's largest product partly dropped (measured:
+// 448^2 plus 63 products of 1 came out 448^2 + 56) and the blocks in fp32;
+// the online softmax runs in fp32 as in the bf16 kernel; the probabilities are
 // rounded to E4M3 for the P.V product, which is the one rounding step that
-// the 16-bit kernel does in bf16.  They are scaled by 448 * 2^-kF8Headroom
-// against a lazily moved reference max (see kF8Headroom), so the largest
-// probability of a row lands between 224 and 448, within the largest code;
-// codes below the normal range carry an absolute error of at most 2^-10,
-// i.e. 2^(kF8Headroom-10) / 448 in probability units.
+// the 16-bit kernel does in bf16.  Each tile's probabilities are coded
+// against their own power-of-two scale, so that the tile's largest lands
+// between 224 and 448, within the largest code (see kF8Headroom); the scale
+// goes to the P.V product as the matrix instruction's block scale of the P
+// operand.  Codes below the normal range carry an absolute error of at most
+// 2^-10, i.e. at most 2^(kF8Headroom-10) / 448 in units of the row's
+// largest probability.
 //
 // Mapping onto CDNA4 (the bf16 kernel's design with 8-bit operands):
 //  * 512 threads = 8 wavefronts of 32 query rows; HG query heads of a GQA
@@ -52,12 +56,18 @@ constexpr int kF8Threads = 512;
 constexpr int kF8Stages = 4;
 constexpr int kF8BN = 64;                  // keys per tile
 constexpr float kLog2E4M3Max = 8.807354922057604f;   // log2(448)
-// Bits of probability between a row's reference max and the largest E4M3
-// value: probabilities are taken as 448 * 2^-kF8Headroom * 2^((s - m) cq)
-// against a reference m that moves only when a tile's max exceeds it by more
-// than kF8Headroom bits, so they never pass 448 and the accumulator is
-// rescaled only on such moves.
+// Bits of probability between a tile's largest probability and the largest
+// E4M3 value.  A row's reference m is the max of its first tile with a
+// visible key.  The probabilities of a tile whose max is mt are coded as
+// 448 * 2^-kF8Headroom * 2^((s - m) cq - k) with k = floor((mt - m) cq), so
+// they never pass 448 and the tile's largest is at least 224; the factor 2^k
+// is the P operand's block scale in P.V (exponent 127 + k) and multiplies
+// the tile's share of the row sum.  Accumulator and row sum thus stay against
+// m; m moves (and they are rescaled) only when a tile's max passes it by more
+// than kF8MaxShift bits, which keeps them far from overflow.  Tiles more
+// than 126 bits below m are coded with k = -126.
 constexpr float kF8Headroom = 1.f;
+constexpr float kF8MaxShift = 32.f;
 
 // Byte tiles (rows x D codes, row-major): 16-byte chunk c of row r sits at
 // position c ^ f8swz(r).  The function depends only on row bits that
@@ -75,6 +85,26 @@ __device__ __forceinline__ int f8swz(int r) {
 // 32x32x64 MFMA on E4M3 operands with unit block scales.
 __device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+// The same with B's block scale 2^(sb - 127) (E8M0 exponent byte sb, 1..254)
+// given per lane: lane l scales column l % 32 over its 32 values of the
+// contraction (probed on the device).
+__device__ __forceinline__ f32x16 mma_f8_sb(i32x8 a, i32x8 b, f32x16 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
+}
+
+// Reference move and block-scale exponent for a tile whose max is mt (see
+// kF8Headroom): on return m0 is the reference to use, mv whether it moved
+// to mt (then acc and l need the factor 2^-x), k the exponent.  Written with
+// selects only: a branch here would split the tile's code.
+__device__ __forceinline__ void f8_plan(float m, float mt, float cq, float& m0, bool& mv, int& k,
+                                        float& x) {
+  const float r = m > kNegInf ? m : mt;   // the first tile with a key sets the reference
+  x = (mt - r) * cq;                      // NaN when neither has a key
+  mv = x > kF8MaxShift;
+  m0 = mv ? mt : r;
+  const int kf = (int)fminf(fmaxf(floorf(x), -126.f), kF8MaxShift);
+  k = mt > kNegInf && !mv ? kf : 0;
 }
 
 // Four fp32 values (already within +-448) to E4M3 codes in one word, in order.
@@ -277,14 +307,10 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
     // Base-2 exponent factor of this row: |scale| * log2(e) * qs_i * ks, and
     // the headroom in raw product units.
     const float cq = fmaxf(p.c * qs * p.kscale[kvplane], 1e-30f);
-    const float hr = kF8Headroom / cq;
 
     const int lim = q0w + 31 + off - 64 * kh;   // last key its rows see, minus its block start
     const int my_tiles = !active ? 0 : CAUSAL ? (lim < 0 ? 0 : min(ntiles, lim / BN + 1)) : ntiles;
-    // A row that sees no key keeps m = -inf, factor 1 and offset 0.  Under
-    // the key split the same holds, tile by tile, for a row whose key half
-    // has shown it no key yet.
-    const bool has_keys = !CAUSAL || my_q + off >= 0;
+    // A row keeps m = -inf and offset 0 until a tile shows it a key.
 
     float m = kNegInf;   // reference max of this row's raw 8-bit products
     float l = 0.f;       // this half-wave's share of the running sum of 448 * P
@@ -350,17 +376,20 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       for (int i = 2; i < 32; i += 2)
         mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
       mt = max_halves8(mt);
-      const float m_new = mt > m + hr ? mt : m;
-      const bool live = KSPLIT ? m_new > kNegInf : has_keys;
-      const float corr = live ? exp2_fast((m - m_new) * cq) : 1.f;
-      if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+      float m0;
+      bool mv;
+      int k;
+      float x;
+      f8_plan(m, mt, cq, m0, mv, k, x);
+      if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+        const float corr = mv ? exp2_fast(-x) : 1.f;
 #pragma unroll
         for (int i = 0; i < ND; ++i) acc[i] *= corr;
+        l *= corr;
       }
-      l *= corr;
-      m = m_new;
-      // 448 * 2^-headroom * P = 2^(s*cq - m*cq + log2 448 - headroom).
-      const float mc = live ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
+      m = m0;
+      // 448 * 2^-headroom * P * 2^-k = 2^(s*cq - m*cq - k + log2 448 - headroom).
+      const float mc = m > kNegInf ? m * cq + (float)k - kLog2E4M3Max + kF8Headroom : 0.f;
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -369,7 +398,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
           s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
           ls[r & 3] += s[kb][r];
         }
-      l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      l += ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), k);
+      const int sb = 127 + k;
       // B operand: byte 4w + i is key block w/4, register 4*(w%4) + i.
       i32x8 pb;
 #pragma unroll
@@ -388,7 +418,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         for (int j = 0; j < 4; ++j) tie(va[db][j]);
         const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
                          (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
-        acc[db] = mma_f8(a, pb, acc[db]);
+        acc[db] = mma_f8_sb(a, pb, acc[db], sb);
       }
       lgkm_wait<0>();
 #pragma unroll
@@ -397,7 +427,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         for (int j = 0; j < 4; ++j) tie(va[db][j]);
         const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
                          (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
-        acc[db] = mma_f8(a, pb, acc[db]);
+        acc[db] = mma_f8_sb(a, pb, acc[db], sb);
       }
     };
     if constexpr (D != 128) {
@@ -416,8 +446,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       // same wavefront.  Tile t+1 must have landed at tile t's barrier:
       // copies run two tiles ahead of it.
       f32x16 sbuf[2][2];                   // scores of tiles t (even/odd) and t+1
-      float m_next = m, corr_next = 1.f;   // the reference move due at tile t+1
-      bool move_next = false;
+      int k_next = 0;                      // tile t+1's block-scale exponent
       auto scores = [&](auto st_c, f32x16 (&s)[2]) __attribute__((always_inline)) {
         constexpr int KT = decltype(st_c)::value * TILE;
         u32x4 kr[2][2 * NC8];
@@ -464,12 +493,19 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         for (int i = 2; i < 32; i += 2)
           mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
         mt = max_halves8(mt);
-        m_next = mt > m + hr ? mt : m;
-        // Under the key split a row whose key half has shown it no key yet
-        // stays at m = -inf, factor 1 and offset 0, tile by tile.
-        const bool live = KSPLIT ? m_next > kNegInf : has_keys;
-        corr_next = live ? exp2_fast((m - m_next) * cq) : 1.f;
-        move_next = __builtin_amdgcn_ballot_w64(m_next > m) != 0;
+        // The reference for tile t+1, and its (rare) move, applied here:
+        // after tile t's P.V, at the end of its step, so that no branch
+        // splits the step's code.
+        float m0, x;
+        bool mv;
+        f8_plan(m, mt, cq, m0, mv, k_next, x);
+        if (__builtin_amdgcn_ballot_w64(mv) != 0) {
+          const float corr = mv ? exp2_fast(-x) : 1.f;
+#pragma unroll
+          for (int i = 0; i < ND; ++i) acc[i] *= corr;
+          l *= corr;
+        }
+        m = m0;
       };
       auto step = [&](int t, auto st_c) __attribute__((always_inline)) {
         constexpr int ST = decltype(st_c)::value;
@@ -480,20 +516,14 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         tile_barrier();
         if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
         if (t >= my_tiles) return;
-        if (move_next) {
-#pragma unroll
-          for (int i = 0; i < ND; ++i) acc[i] *= corr_next;
-        }
-        l *= corr_next;
-        m = m_next;
+        const int k = k_next;
         scores(IC<(ST + 1) % STAGES>{}, sbuf[CUR ^ 1]);
         u32x2 va[ND][4];
         static_for<0, ND>([&](auto db_c) {
           static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
         });
-        // 448 * 2^-headroom * P = 2^(s*cq - m*cq + log2 448 - headroom).
-        const bool live = KSPLIT ? m > kNegInf : has_keys;
-        const float mc = live ? m * cq - kLog2E4M3Max + kF8Headroom : 0.f;
+        // 448 * 2^-headroom * P * 2^-k = 2^(s*cq - m*cq - k + log2 448 - headroom).
+        const float mc = m > kNegInf ? m * cq + (float)k - kLog2E4M3Max + kF8Headroom : 0.f;
         f32x16 (&s)[2] = sbuf[CUR];
         float ls[4];
 #pragma unroll
@@ -503,7 +533,8 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
             s[kb][r] = exp2_fast(fmaf(s[kb][r], cq, -mc));
             ls[r & 3] = kb == 0 && r < 4 ? s[kb][r] : ls[r & 3] + s[kb][r];
           }
-        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l += ldexpf((ls[0] + ls[1]) + (ls[2] + ls[3]), k);
+        const int sb = 127 + k;
         i32x8 pb;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
@@ -517,7 +548,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
           for (int j = 0; j < 4; ++j) tie(va[db][j]);
           const i32x8 a = {(int)va[db][0][0], (int)va[db][0][1], (int)va[db][1][0], (int)va[db][1][1],
                            (int)va[db][2][0], (int)va[db][2][1], (int)va[db][3][0], (int)va[db][3][1]};
-          acc[db] = mma_f8(a, pb, acc[db]);
+          acc[db] = mma_f8_sb(a, pb, acc[db], sb);
         }
         decide(t + 1, sbuf[CUR ^ 1]);
       };

@@ -125,11 +125,16 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * (one scale per kv head).  Scales must be positive and finite.  Computes
  * exactly what fa_fwd computes for those inputs (same causal modes 0/1/2,
  * any finite scale), with this arithmetic: q.k products of the codes are
- * exact and summed in fp32 on the 8-bit matrix cores; the online softmax is
- * fp32; each probability, times 448, is rounded to E4M3 (relative error at
- * most 2^-4, absolute at most 2^-10/448 near zero) for the p.v product,
- * which sums in fp32; the row sum uses the unrounded probabilities; o is
- * rounded to bf16.  Errors: as fa_fwd, and FA_ERR_NULL for a NULL scale
+ * exact; the 8-bit matrix cores add each block of 64 of them with terms far
+ * below the block's largest product partly dropped (on the device, a block
+ * of one product of 448^2 and 63 of 1 summed to 448^2 + 56), and the blocks
+ * in fp32; the online softmax is
+ * fp32; each key tile's probabilities are scaled by a power of two that
+ * puts the tile's largest in [224, 448) and rounded to E4M3 (relative error
+ * at most 2^-4, absolute at most 2^-9/448 of the row's largest probability)
+ * for the p.v product, which applies the power of two as the matrix
+ * instruction's block scale and sums in fp32; the row sum uses the
+ * unrounded probabilities; o is rounded to bf16.  Errors: as fa_fwd, and FA_ERR_NULL for a NULL scale
  * array on a non-empty call.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* qscale,

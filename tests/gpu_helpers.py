@@ -236,10 +236,12 @@ def decode_error_bound(q, K, V, seqlens, *, safety=1.25):
 # 8-bit forward: element-wise error bound
 # ---------------------------------------------------------------------------
 E4M3_U = 2.0 ** -4            # relative rounding of an E4M3 normal value (3 mantissa bits)
-F8_HEADROOM = 1                # bits between a row's reference max and the largest E4M3 code
+F8_HEADROOM = 1                # bits between a tile's largest probability and the largest E4M3 code
 # Absolute rounding of a probability code below the smallest normal, in P
-# units: the kernel codes 448 * 2^-F8_HEADROOM * P against a reference at
-# most the row's max, and a subnormal code rounds by at most 2^-10.
+# units: the kernel codes each tile's probabilities with a power-of-two
+# factor that puts the tile's largest between 448 * 2^-F8_HEADROOM and 448,
+# i.e. a factor of at least 448 * 2^-F8_HEADROOM per unit of P (no tile's
+# max exceeds the row's), and a subnormal code rounds by at most 2^-10.
 E4M3_FLOOR = 2.0 ** (F8_HEADROOM - 10) / 448
 
 
@@ -247,9 +249,9 @@ def fp8_fwd_error_bound(q, k, v, *, causal, scale, causal_off=0, safety=1.25):
     """Bound on |O_kernel - O_exact| for fa_fwd_fp8, element by element.
 
     q, k, v: the dequantised fp64 inputs.  The only rounding of consequence
-    is that of each probability P_ij = exp(s_ij - m_i) <= 1 (coded as 448 *
-    2^-F8_HEADROOM * P against a reference at most m_i) to E4M3 before the P.V
-    product: |dP| <= max(2^-4 P, E4M3_FLOOR).  With the row sum
+    is that of each probability P_ij = exp(s_ij - m_i) <= 1 (coded with a
+    per-tile power-of-two factor of at least 448 * 2^-F8_HEADROOM) to E4M3
+    before the P.V product: |dP| <= max(2^-4 P, E4M3_FLOOR).  With the row sum
     l_i = sum_j P_ij unrounded,
         |O_err[i, c]| <= sum_j max(2^-4 P_ij, E4M3_FLOOR) |v_jc| / l_i,
     plus the bf16 rounding of O (2^-8 |O|); times `safety`, plus 1e-6."""

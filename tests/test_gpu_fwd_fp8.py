@@ -4,7 +4,7 @@ dequantised inputs, through the C ABI.
 
 Bar (element-wise, derived from the kernel's arithmetic in
 gpu_helpers.fp8_fwd_error_bound): the probabilities are the one quantity
-rounded to 8 bits, so |O err| <= 1.25 * (sum_j max(2^-4 P_ij, 2^-10/448)
+rounded to 8 bits, so |O err| <= 1.25 * (sum_j max(2^-4 P_ij, 2^-9/448)
 |v_j| / l_i + 2^-8 |O_i|); lse <= 1e-3 (the scores are exact products).
 """
 import numpy as np
@@ -112,6 +112,44 @@ def test_fp8_peaked_rows():
     """Q x 3 (the Qwen3-shaped workload's distribution)."""
     parity(inputs.Prefill("t", B=1, Hq=4, Hkv=2, Tq=300, Tk=300, d=128, causal=True, q_mult=3.0,
                           seed=44))
+
+
+@pytest.mark.parametrize("d,growth,causal", [(128, 12.0, True), (128, 40.0, True), (64, 40.0, True),
+                                              (128, -12.0, True), (64, -3.0, True), (128, 40.0, False),
+                                              (64, -40.0, False)])
+def test_fp8_tile_scales_far_from_reference(d, growth, causal):
+    """Scores that move along the key sequence by about `growth` powers of 2
+    per 64 keys, up or down.  Each tile's probabilities are coded against
+    the row's first reference shifted by the tile's own power-of-two block
+    scale: rising rows pass the reference by more than the 32-bit guard
+    (growth 40: on every tile; growth 12: every few tiles), which moves the
+    reference and rescales the accumulator; falling rows put later tiles far
+    below it (past the clamp at -126 bits).  Scores reach hundreds of bits,
+    so each is a single product (q and k nonzero only in dimension 0): the
+    matrix core then adds nothing but zeros to it and the score is exact,
+    which keeps this test about the tile scaling (the matrix core does not
+    sum a 64-element 8-bit block of mixed magnitudes exactly, and at
+    hundreds of bits that error alone would pass the lse bar).  Every
+    element against the derived bound, lse <= 1e-3."""
+    rng = np.random.default_rng(17)
+    Tq = Tk = 1000
+    scale = 1.0 / np.sqrt(d)
+    c = scale * np.log2(np.e)
+    slope = growth / (64.0 * c)
+    q = np.zeros((1, 2, Tq, d), np.float32)
+    q[..., 0] = 1.0 + 0.25 * rng.standard_normal((1, 2, Tq)).astype(np.float32)
+    k = np.zeros((1, 1, Tk, d), np.float32)
+    k[..., 0] = slope * np.arange(Tk, dtype=np.float32) + rng.standard_normal((1, 1, Tk)).astype(np.float32)
+    v = rng.standard_normal((1, 1, Tk, d)).astype(np.float32)
+    q8, qs = inputs.quantize_rows_e4m3(q)
+    k8, ks = inputs.quantize_blocks_e4m3(k, 2)
+    v8, vs = inputs.quantize_blocks_e4m3(v, 2)
+    say("fa_fwd_fp8 moving scores d", d, "growth", growth, "causal", causal)
+    O, L = run_fp8(q8, k8, v8, qs, ks, vs, 1 if causal else 0, scale)
+    qd, kd, vd = oracle.fp8_attention_inputs(q8, k8, v8, qs, ks, vs)
+    Or, Lr = oracle.softmax_attention(qd, kd, vd, causal=causal, scale=scale)
+    check_bounded(O, Or, fp8_fwd_error_bound(qd, kd, vd, causal=causal, scale=scale))
+    check("lse", L, Lr, BF16_LSE_TOL)
 
 
 def test_fp8_qwen3_shape_full():
