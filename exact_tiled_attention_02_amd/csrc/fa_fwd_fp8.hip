@@ -103,8 +103,10 @@ __device__ __forceinline__ void f8_plan(float m, float mt, float cq, float& m0, 
   x = (mt - r) * cq;                      // NaN when neither has a key
   mv = x > kF8MaxShift;
   m0 = mv ? mt : r;
-  const int kf = (int)fminf(fmaxf(floorf(x), -126.f), kF8MaxShift);
-  k = mt > kNegInf && !mv ? kf : 0;
+  // Without a move x <= kF8MaxShift; a tile with no key (x = -inf or NaN)
+  // gets -126, harmless since all its probabilities are 0.
+  const int kf = (int)fmaxf(floorf(x), -126.f);
+  k = mv ? 0 : kf;
 }
 
 // Four fp32 values (already within +-448) to E4M3 codes in one word, in order.
