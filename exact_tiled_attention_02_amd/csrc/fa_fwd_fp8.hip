@@ -68,6 +68,7 @@ constexpr float kLog2E4M3Max = 8.807354922057604f;   // log2(448)
 // than 126 bits below m are coded with k = -126.
 constexpr float kF8Headroom = 1.f;
 constexpr float kF8MaxShift = 32.f;
+constexpr float kF8Offset = kF8Headroom - kLog2E4M3Max;   // one constant in the exponent offset
 
 // Byte tiles (rows x D codes, row-major): 16-byte chunk c of row r sits at
 // position c ^ f8swz(r).  The function depends only on row bits that
@@ -110,9 +111,15 @@ __device__ __forceinline__ void f8_plan(float m, float mt, float cq, float& m0, 
 }
 
 // Four fp32 values (already within +-448) to E4M3 codes in one word, in order.
+// The conversion writes one half of its destination and keeps the other;
+// both halves are written here, so the word starts from an opaque value
+// (an empty statement) rather than from a zero the compiler would have to
+// move into it first.
 __device__ __forceinline__ int pack_e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+  int w;
+  asm volatile("" : "=v"(w));
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
 __device__ __forceinline__ float max_halves8(float x) {
@@ -391,7 +398,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       }
       m = m0;
       // 448 * 2^-headroom * P * 2^-k = 2^(s*cq - m*cq - k + log2 448 - headroom).
-      const float mc = m > kNegInf ? m * cq + (float)k - kLog2E4M3Max + kF8Headroom : 0.f;
+      const float mc = m > kNegInf ? fmaf(m, cq, (float)k + kF8Offset) : 0.f;
       float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -525,7 +532,7 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
           static_for<0, 4>([&](auto j_c) { va[db_c][j_c] = lds_read_tr8<VT + 16 * j_c * D>(vread[db_c]); });
         });
         // 448 * 2^-headroom * P * 2^-k = 2^(s*cq - m*cq - k + log2 448 - headroom).
-        const float mc = m > kNegInf ? m * cq + (float)k - kLog2E4M3Max + kF8Headroom : 0.f;
+        const float mc = m > kNegInf ? fmaf(m, cq, (float)k + kF8Offset) : 0.f;
         f32x16 (&s)[2] = sbuf[CUR];
         float ls[4];
 #pragma unroll
