@@ -358,6 +358,14 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
     float m = kNegInf;   // running max of this row's raw scores
     float nmc = 0.f;
     float thr = kNegInf;
+    // At d = 128 the score products start from minus the reference (raw
+    // units; 0 until the row has seen a key) instead of 0, so that the
+    // exponent argument is one multiplication, s' * c, rather than an FMA.
+    constexpr bool SHIFT = D == 128;
+    float nref = 0.f;
+    f32x16 sinit;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sinit[r] = 0.f;
     float l = 0.f;       // this half-wave's share of the running sum
     f32x16 acc[ND];
 #pragma unroll
@@ -398,7 +406,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
           constexpr int I = decltype(i_c)::value;
           constexpr int AFTER = I + PF <= NF ? PF - 1 : NF - 1 - I;
           lds_wait_tie<AFTER>(kf[I]);
-          s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? f32x16{} : s[I & 1]);
+          s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? (SHIFT ? sinit : f32x16{}) : s[I & 1]);
           if constexpr (I + PF < NF) read_k(IC<I + PF>{});
         });
       }
@@ -424,6 +432,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
       for (int i = 2; i < 32; i += 2)
         mt = fmaxf(fmaxf(mt, s[i >> 4][i & 15]), s[(i + 1) >> 4][(i + 1) & 15]);
       mt = max_halves(mt);
+      if constexpr (SHIFT) mt -= nref;   // back to raw units
 
       // Online update.  The running max m is exact; the reference the
       // probabilities are taken against moves to it only when some row of
@@ -442,7 +451,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
         // probability so far (see top_fix).
         const bool seen = m_prev > kNegInf;
         const float corr = seen ? exp2_fast(nmc_new - nmc) : 0.f;
-        const float fold = seen ? top_fix(exp2_fast(fmaf(m_prev, c, nmc))) : 1.f;
+        const float fold = seen ? top_fix(exp2_fast(SHIFT ? (m_prev + nref) * c : fmaf(m_prev, c, nmc))) : 1.f;
         const float f = corr * fold;
         if (__builtin_amdgcn_ballot_w64(seen) != 0) {   // else acc is still 0
 #pragma unroll
@@ -451,13 +460,26 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
         l *= corr;
         nmc = nmc_new;
         thr = m + lazy_raw;
+        if constexpr (SHIFT) {
+          // This tile's scores were shifted by the old reference: move them
+          // to the new one, and start the next tiles' products from it.
+          const float nref_new = m > kNegInf ? -m : 0.f;
+          const float dlt = nref_new - nref;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] += dlt;
+          nref = nref_new;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sinit[r] = nref;
+        }
       }
       float ls[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          s[kb][r] = exp2_fast(fmaf(s[kb][r], c, nmc));
+          s[kb][r] = exp2_fast(SHIFT ? s[kb][r] * c : fmaf(s[kb][r], c, nmc));
           ls[r & 3] = kb == 0 && r < 4 ? s[kb][r] : ls[r & 3] + s[kb][r];   // four partial sums
         }
       l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -521,7 +543,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
 
     // The bf16 rounding of the row's largest probability, undone (top_fix):
     // folded into the final scale, or applied before the key halves merge.
-    const float fix = m > kNegInf ? top_fix(exp2_fast(fmaf(m, c, nmc))) : 1.f;
+    const float fix = m > kNegInf ? top_fix(exp2_fast(SHIFT ? (m + nref) * c : fmaf(m, c, nmc))) : 1.f;
     if constexpr (KSPLIT) {
 #pragma unroll
       for (int i = 0; i < ND; ++i) acc[i] *= fix;
