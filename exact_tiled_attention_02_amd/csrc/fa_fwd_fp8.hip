@@ -338,28 +338,28 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       tile_barrier();
       if (t + STAGES - 1 < ntiles) issue_copies(t + STAGES - 1);
       if (t >= my_tiles) return;
-      // S^T for the two 32-key blocks.
+      // S^T for the two 32-key blocks: K reads in the order the products
+      // consume them, each product waiting only for its own two.
+      constexpr int NP = 2 * NC8;   // products
       u32x4 kr[2][2 * NC8];
-      static_for<0, 2 * NC8>([&](auto i_c) {
-        kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
-        kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
+      static_for<0, 2>([&](auto kb_c) {
+        static_for<0, 2 * NC8>([&](auto i_c) {
+          kr[kb_c][i_c] = lds_read_u32x4<KT + decltype(kb_c)::value * 32 * D>(kread[i_c]);
+        });
       });
-      lgkm_wait<0>();
-#pragma unroll
-      for (int i = 0; i < 2 * NC8; ++i) {
-        tie(kr[0][i]);
-        tie(kr[1][i]);
-      }
-      f32x16 s[2] = {};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < NC8; ++c) {
-          const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
-          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-          s[kb] = mma_f8(a, qf[c], s[kb]);
-        }
+      f32x16 s[2];
+      static_for<0, NP>([&](auto j_c) {
+        constexpr int J = decltype(j_c)::value;
+        constexpr int KB = J / NC8, C = J % NC8;
+        lgkm_wait<2 * (NP - 1 - J)>();
+        tie(kr[KB][2 * C]);
+        tie(kr[KB][2 * C + 1]);
+        const u32x4 a0 = kr[KB][2 * C], a1 = kr[KB][2 * C + 1];
+        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[KB] = mma_f8(a, qf[C], C == 0 ? f32x16{} : s[KB]);
+        __builtin_amdgcn_sched_barrier(0);   // issued before the next wait
+      });
 
       // V^T reads for the first half of the output blocks go out now; they do
       // not depend on the probabilities.
@@ -458,28 +458,28 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       int k_next = 0;                      // tile t+1's block-scale exponent
       auto scores = [&](auto st_c, f32x16 (&s)[2]) __attribute__((always_inline)) {
         constexpr int KT = decltype(st_c)::value * TILE;
+        // K reads in the order the products consume them, each product
+        // waiting only for its own two (the first product starts while the
+        // other reads are still in flight).
+        constexpr int NP = 2 * NC8;   // products
         u32x4 kr[2][2 * NC8];
-        static_for<0, 2 * NC8>([&](auto i_c) {
-          kr[0][i_c] = lds_read_u32x4<KT>(kread[i_c]);
-          kr[1][i_c] = lds_read_u32x4<KT + 32 * D>(kread[i_c]);
+        static_for<0, 2>([&](auto kb_c) {
+          static_for<0, 2 * NC8>([&](auto i_c) {
+            kr[kb_c][i_c] = lds_read_u32x4<KT + decltype(kb_c)::value * 32 * D>(kread[i_c]);
+          });
         });
-        lgkm_wait<0>();
-#pragma unroll
-        for (int i = 0; i < 2 * NC8; ++i) {
-          tie(kr[0][i]);
-          tie(kr[1][i]);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[kb] = f32x16{};
-#pragma unroll
-          for (int c = 0; c < NC8; ++c) {
-            const u32x4 a0 = kr[kb][2 * c], a1 = kr[kb][2 * c + 1];
-            const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                             (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-            s[kb] = mma_f8(a, qf[c], s[kb]);
-          }
-        }
+        static_for<0, NP>([&](auto j_c) {
+          constexpr int J = decltype(j_c)::value;
+          constexpr int KB = J / NC8, C = J % NC8;
+          lgkm_wait<2 * (NP - 1 - J)>();
+          tie(kr[KB][2 * C]);
+          tie(kr[KB][2 * C + 1]);
+          const u32x4 a0 = kr[KB][2 * C], a1 = kr[KB][2 * C + 1];
+          const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+          s[KB] = mma_f8(a, qf[C], C == 0 ? f32x16{} : s[KB]);
+          __builtin_amdgcn_sched_barrier(0);   // issued before the next wait
+        });
       };
       // Mask tile t's scores, take its max and decide the reference move.
       // Tiles past this wavefront's last (formed on stale stage data) are
