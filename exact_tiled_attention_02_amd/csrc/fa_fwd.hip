@@ -407,6 +407,7 @@ __global__ void __launch_bounds__(kFwdThreads, 1) fwd_bf16_kernel(const FwdParam
           constexpr int AFTER = I + PF <= NF ? PF - 1 : NF - 1 - I;
           lds_wait_tie<AFTER>(kf[I]);
           s[I & 1] = mma_32x32x16(kf[I], qf[I >> 1], I < 2 ? (SHIFT ? sinit : f32x16{}) : s[I & 1]);
+          __builtin_amdgcn_sched_barrier(0);   // issued before the next wait, not sunk past it
           if constexpr (I + PF < NF) read_k(IC<I + PF>{});
         });
       }
