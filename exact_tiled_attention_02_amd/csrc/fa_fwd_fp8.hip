@@ -342,15 +342,17 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
       // consume them, each product waiting only for its own two.
       constexpr int NP = 2 * NC8;   // products
       u32x4 kr[2][2 * NC8];
-      static_for<0, 2>([&](auto kb_c) {
-        static_for<0, 2 * NC8>([&](auto i_c) {
-          kr[kb_c][i_c] = lds_read_u32x4<KT + decltype(kb_c)::value * 32 * D>(kread[i_c]);
-        });
+      static_for<0, NP>([&](auto j_c) {
+        constexpr int KB = decltype(j_c)::value & 1, C = decltype(j_c)::value >> 1;
+        kr[KB][2 * C] = lds_read_u32x4<KT + KB * 32 * D>(kread[2 * C]);
+        kr[KB][2 * C + 1] = lds_read_u32x4<KT + KB * 32 * D>(kread[2 * C + 1]);
       });
+      // Products alternate between the two key blocks (no product waits on
+      // the accumulator of the one just before it).
       f32x16 s[2];
       static_for<0, NP>([&](auto j_c) {
         constexpr int J = decltype(j_c)::value;
-        constexpr int KB = J / NC8, C = J % NC8;
+        constexpr int KB = J & 1, C = J >> 1;
         lgkm_wait<2 * (NP - 1 - J)>();
         tie(kr[KB][2 * C]);
         tie(kr[KB][2 * C + 1]);
@@ -463,14 +465,16 @@ __global__ void __launch_bounds__(kF8Threads, 1) fwd_fp8_kernel(const FwdParams 
         // other reads are still in flight).
         constexpr int NP = 2 * NC8;   // products
         u32x4 kr[2][2 * NC8];
-        static_for<0, 2>([&](auto kb_c) {
-          static_for<0, 2 * NC8>([&](auto i_c) {
-            kr[kb_c][i_c] = lds_read_u32x4<KT + decltype(kb_c)::value * 32 * D>(kread[i_c]);
-          });
+        static_for<0, NP>([&](auto j_c) {
+          constexpr int KB = decltype(j_c)::value & 1, C = decltype(j_c)::value >> 1;
+          kr[KB][2 * C] = lds_read_u32x4<KT + KB * 32 * D>(kread[2 * C]);
+          kr[KB][2 * C + 1] = lds_read_u32x4<KT + KB * 32 * D>(kread[2 * C + 1]);
         });
+        // Products alternate between the two key blocks, so that no product
+        // waits on the accumulator of the one just before it.
         static_for<0, NP>([&](auto j_c) {
           constexpr int J = decltype(j_c)::value;
-          constexpr int KB = J / NC8, C = J % NC8;
+          constexpr int KB = J & 1, C = J >> 1;
           lgkm_wait<2 * (NP - 1 - J)>();
           tie(kr[KB][2 * C]);
           tie(kr[KB][2 * C + 1]);
