@@ -38,6 +38,14 @@
  *    and the outputs must not be used.
  *  - Device addresses are not validated beyond non-NULL: passing buffers
  *    smaller than the stated shapes is undefined behaviour.
+ *  - HIP graphs: fa_fwd, fa_fwd_f32, fa_fwd_fp8 and fa_decode_noalloc
+ *    allocate nothing and enqueue only kernel launches (no memset, no copy),
+ *    so a stream capture of them replays like the calls themselves; the
+ *    graph keeps the pointers it was captured with and reads the inputs at
+ *    each replay.  Make one eager fa_decode_noalloc call on the device
+ *    before capturing it (its first call looks up the workspace's device
+ *    address).  fa_decode, its 8-bit forms and fa_bwd may grow their
+ *    workspace with stream-ordered allocation and are not meant for capture.
  */
 #ifndef FA_H_
 #define FA_H_
