@@ -310,11 +310,14 @@ def test_slowly_growing_row_max(d, growth):
     check("lse", L, Lr, BF16_LSE_TOL)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.5])
-def test_other_scales(scale):
-    w = inputs.Prefill("t", B=1, Hq=2, Hkv=1, Tq=150, Tk=150, d=64, causal=True, seed=4)
+def test_other_scales(scale, d):
+    """Negative, zero and large scales; at d = 128 the score products start
+    from minus the reference, at d = 64 from zero."""
+    w = inputs.Prefill("t", B=1, Hq=2, Hkv=1, Tq=150, Tk=150, d=d, causal=True, seed=4)
     q, k, v = inputs.prefill_inputs(w)
-    say("fa_fwd bf16 scale", scale)
+    say("fa_fwd bf16 scale", scale, "d", d)
     O, L = run_bf16(q, k, v, True, scale)
     Or, Lr = oracle.softmax_attention(q, k, v, causal=True, scale=scale)
     check("O", O, Or, BF16_O_TOL)
